@@ -1,0 +1,135 @@
+/*
+ * q4g128.h -- C ABI of the int4 group-128 weight-streaming GEMV library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Weight format (rumik-oss-1 int4 write-up, rtts.neoandmatrix.me, section
+ * "Step 3: an int4 file and a first kernel on the laptop"): a projection
+ * matrix W with N output rows and K input columns is quantised in groups of
+ * 128 consecutive columns of each row; every group has one fp16 scale and
+ * one fp16 minimum, and two 4-bit codes share one byte.  The dequantised
+ * weight is
+ *
+ *     w[n][k] = code[n][k] * scale[n][k / 128] + min[n][k / 128].
+ *
+ * Canonical layout used by every entry point (readings of the format that
+ * the pages leave open are stated here once):
+ *   packed  uint8  [N][K/2]  row-major; byte j of row n holds code[n][2j] in
+ *                            bits 0..3 and code[n][2j+1] in bits 4..7.
+ *   scales  uint16 [N][K/128] row-major fp16 bit patterns.
+ *   mins    uint16 [N][K/128] row-major fp16 bit patterns.
+ *   x / X   uint16 [B][K]    row-major fp16 bit patterns, one activation
+ *                            vector (request or prompt token) per row.
+ *   y / Y   float  [B][N]    row-major fp32 results; Y = X * W^T.
+ *
+ * Ownership and execution model (all entry points):
+ *   - Every pointer is DEVICE memory owned by the caller.  The library never
+ *     allocates, frees or keeps a pointer after returning, and needs no
+ *     workspace.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     work; they never synchronise the host.  Buffers must stay alive until
+ *     the enqueued work completes.
+ *   - Outputs are fully overwritten and must not overlap any input.
+ *   - Arguments are validated on the host before any HIP call; an invalid
+ *     call enqueues nothing.
+ *   - Results are deterministic: no atomics, fixed reduction orders.
+ *
+ * Limits: 1 <= N <= 2^31 - 256; K a multiple of 128 with 128 <= K <= 32768;
+ * batch / prompt rows at most 2^31 - 256.
+ */
+#ifndef Q4G128_H
+#define Q4G128_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t q4_status;
+
+/* Only the entry points below are exported from libq4g128.so. */
+#define Q4_API __attribute__((visibility("default")))
+
+#define Q4_OK 0
+/* NULL pointer, N <= 0, B outside [1, 16], M <= 0, or an output that
+   overlaps an input. */
+#define Q4_EINVAL (-1)
+/* K not a positive multiple of 128, K above 32768, or N / M above
+   Q4G128_MAX_N. */
+#define Q4_ESHAPE (-2)
+/* codes / packed / x / X not 16-byte aligned; scales / mins not 2-byte
+   aligned; y / Y not 4-byte aligned. */
+#define Q4_EALIGN (-3)
+/* The HIP runtime reported an error while querying the device or launching;
+   q4g128_last_hip_error() returns the hipError_t of the calling thread. */
+#define Q4_EDEVICE (-4)
+
+#define Q4G128_GROUP 128
+#define Q4G128_MAX_K 32768
+#define Q4G128_MAX_BATCH 16
+#define Q4G128_MAX_N 0x7FFFFF00LL
+
+/*
+ * q4g128_pack -- two codes per byte.
+ *   codes  [N][K] uint8, only the low 4 bits of each code are used.
+ *   packed [N][K/2] uint8, written.
+ * The export step of the rumik write-up ("Step 3": a short CPU job wrote the
+ * int4 file) in device form; untimed set-up, not part of the decode step.
+ */
+Q4_API q4_status q4g128_pack(const uint8_t* codes, uint8_t* packed,
+                      int64_t n, int64_t k, void* stream);
+
+/*
+ * q4g128_gemv -- y[n] = sum_k w[n][k] * x[k]   (batch-1 decode product).
+ * The operation that dominates batch-1 decoding in the rumik write-up
+ * ("Step 3" and "Step 7: why the GEMV was stuck, and a CUDA kernel"): the
+ * packed weights are streamed once, dequantised in registers and multiplied
+ * by the fp16 activation vector with fp32 accumulation.
+ *   packed [N][K/2], scales [N][K/128], mins [N][K/128], x [K] -> y [N] fp32.
+ */
+Q4_API q4_status q4g128_gemv(const uint8_t* packed, const uint16_t* scales,
+                      const uint16_t* mins, const uint16_t* x, float* y,
+                      int64_t n, int64_t k, void* stream);
+
+/*
+ * q4g128_gemm_small_batch -- Y[b][n] = sum_k w[n][k] * X[b][k], 1 <= B <= 16.
+ * Continuous request batching ("Adding GPU backends to a pure-C TTS engine:
+ * Metal, CUDA, and the rented-Mac trick", batching passage): each weight row
+ * is read once and used for all B requests.  Row b of Y is bit-identical to
+ * q4g128_gemv(X[b]) on the same weights (the same page's lesson on matching
+ * the single-stream accumulation order): the arithmetic per output depends
+ * on (N, K) only, never on B.
+ *   X [B][K] fp16 -> Y [B][N] fp32.
+ */
+Q4_API q4_status q4g128_gemm_small_batch(const uint8_t* packed, const uint16_t* scales,
+                                  const uint16_t* mins, const uint16_t* X, float* Y,
+                                  int64_t n, int64_t k, int64_t b, void* stream);
+
+/*
+ * q4g128_gemm_prefill -- Y[m][n] = sum_k w[n][k] * X[m][k] for M prompt
+ * tokens (rumik write-up, "Step 8: a prefill that stays int4": the weights
+ * stay int4 in memory and are unpacked on chip for a matrix-core product).
+ * Each weight is dequantised on chip to fp16, fp16(code*scale + min) with
+ * one rounding, and contracted with the fp16 activations on the gfx950
+ * matrix cores with fp32 accumulation.  M is a runtime argument (any
+ * M >= 1, no re-specialisation per M).  Results agree with the exact
+ * product to the fp16 rounding of w; they are not bit-identical to
+ * q4g128_gemv.
+ *   X [M][K] fp16 -> Y [M][N] fp32.
+ */
+Q4_API q4_status q4g128_gemm_prefill(const uint8_t* packed, const uint16_t* scales,
+                              const uint16_t* mins, const uint16_t* X, float* Y,
+                              int64_t n, int64_t k, int64_t m, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+Q4_API const char* q4g128_status_string(q4_status status);
+
+/* hipError_t recorded by the last Q4_EDEVICE return on the calling thread
+   (0 if none). */
+Q4_API int32_t q4g128_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4G128_H */

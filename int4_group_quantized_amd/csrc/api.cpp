@@ -1,0 +1,165 @@
+// C ABI of the int4 group-128 library: argument validation (host only, no
+// HIP call before it passes), per-device properties, dispatch to the kernel
+// launchers and status reporting.
+#include "q4g128.h"
+
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+q4::DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+q4_status device_error(hipError_t e) {
+    g_last_hip_error = (int32_t)e;
+    (void)hipGetLastError();  // clear the sticky per-thread error for the caller
+    return Q4_EDEVICE;
+}
+
+// Properties of the current device, queried once per device.
+q4_status current_device(q4::DeviceInfo* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_error(e);
+    if (dev < 0 || dev >= kMaxDevices) return device_error(hipErrorInvalidDevice);
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    q4::DeviceInfo& d = g_dev[dev];
+    if (d.device != dev) {
+        int cu = 0, lds = 0, lds_optin = 0;
+        e = hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return device_error(e);
+        e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+        if (e != hipSuccess) return device_error(e);
+        if (hipDeviceGetAttribute(&lds_optin, hipDeviceAttributeSharedMemPerBlockOptin, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            lds_optin = 0;
+        }
+        d.num_cu = cu;
+        d.max_lds = (size_t)(lds_optin > lds ? lds_optin : lds);
+        d.device = dev;
+    }
+    *out = d;
+    return Q4_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+q4_status check_nk(int64_t n, int64_t k) {
+    if (n <= 0) return Q4_EINVAL;
+    if (k < Q4G128_GROUP || k % Q4G128_GROUP != 0 || k > Q4G128_MAX_K) return Q4_ESHAPE;
+    if (n > Q4G128_MAX_N) return Q4_ESHAPE;
+    return Q4_OK;
+}
+
+// Shared checks of the three product entry points; `rows` = B or M.
+q4_status check_product(const uint8_t* packed, const uint16_t* scales, const uint16_t* mins,
+                        const uint16_t* X, const float* Y, int64_t n, int64_t k, int64_t rows) {
+    if (!packed || !scales || !mins || !X || !Y) return Q4_EINVAL;
+    q4_status s = check_nk(n, k);
+    if (s != Q4_OK) return s;
+    if (rows > Q4G128_MAX_N) return Q4_ESHAPE;
+    if (!aligned(packed, 16) || !aligned(X, 16) || !aligned(scales, 2) || !aligned(mins, 2) ||
+        !aligned(Y, 4))
+        return Q4_EALIGN;
+    const size_t g = (size_t)(k / Q4G128_GROUP);
+    const size_t ybytes = (size_t)rows * (size_t)n * sizeof(float);
+    if (overlaps(Y, ybytes, packed, (size_t)n * (size_t)k / 2) ||
+        overlaps(Y, ybytes, scales, (size_t)n * g * 2) || overlaps(Y, ybytes, mins, (size_t)n * g * 2) ||
+        overlaps(Y, ybytes, X, (size_t)rows * (size_t)k * 2))
+        return Q4_EINVAL;
+    return Q4_OK;
+}
+
+q4::GemvArgs make_args(const uint8_t* packed, const uint16_t* scales, const uint16_t* mins,
+                       const uint16_t* x, float* y, int64_t n, int64_t k) {
+    q4::GemvArgs a;
+    a.packed = packed;
+    a.scales = scales;
+    a.mins = mins;
+    a.x = x;
+    a.y = y;
+    a.n = (int)n;
+    a.k = (int)k;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+q4_status q4g128_pack(const uint8_t* codes, uint8_t* packed, int64_t n, int64_t k, void* stream) {
+    if (!codes || !packed) return Q4_EINVAL;
+    q4_status s = check_nk(n, k);
+    if (s != Q4_OK) return s;
+    if (!aligned(codes, 16) || !aligned(packed, 16)) return Q4_EALIGN;
+    if (overlaps(packed, (size_t)n * (size_t)k / 2, codes, (size_t)n * (size_t)k)) return Q4_EINVAL;
+    hipError_t e = q4::launch_pack(codes, packed, n, k, (hipStream_t)stream);
+    return e == hipSuccess ? Q4_OK : device_error(e);
+}
+
+q4_status q4g128_gemv(const uint8_t* packed, const uint16_t* scales, const uint16_t* mins,
+                      const uint16_t* x, float* y, int64_t n, int64_t k, void* stream) {
+    q4_status s = check_product(packed, scales, mins, x, y, n, k, 1);
+    if (s != Q4_OK) return s;
+    q4::DeviceInfo dev;
+    s = current_device(&dev);
+    if (s != Q4_OK) return s;
+    hipError_t e = q4::launch_gemv(make_args(packed, scales, mins, x, y, n, k), dev, (hipStream_t)stream);
+    return e == hipSuccess ? Q4_OK : device_error(e);
+}
+
+q4_status q4g128_gemm_small_batch(const uint8_t* packed, const uint16_t* scales, const uint16_t* mins,
+                                  const uint16_t* X, float* Y, int64_t n, int64_t k, int64_t b,
+                                  void* stream) {
+    if (b < 1 || b > Q4G128_MAX_BATCH) return Q4_EINVAL;
+    q4_status s = check_product(packed, scales, mins, X, Y, n, k, b);
+    if (s != Q4_OK) return s;
+    q4::DeviceInfo dev;
+    s = current_device(&dev);
+    if (s != Q4_OK) return s;
+    hipError_t e = q4::launch_small_batch(make_args(packed, scales, mins, X, Y, n, k), X, Y, (int)b, dev,
+                                          (hipStream_t)stream);
+    return e == hipSuccess ? Q4_OK : device_error(e);
+}
+
+q4_status q4g128_gemm_prefill(const uint8_t* packed, const uint16_t* scales, const uint16_t* mins,
+                              const uint16_t* X, float* Y, int64_t n, int64_t k, int64_t m,
+                              void* stream) {
+    if (m < 1) return Q4_EINVAL;
+    q4_status s = check_product(packed, scales, mins, X, Y, n, k, m);
+    if (s != Q4_OK) return s;
+    if (((n + 63) / 64) * ((m + 15) / 16) > 0x7FFFFFFFLL) return Q4_ESHAPE;
+    q4::DeviceInfo dev;
+    s = current_device(&dev);
+    if (s != Q4_OK) return s;
+    hipError_t e = q4::launch_prefill(make_args(packed, scales, mins, X, Y, n, k), X, Y, (int)m, dev,
+                                      (hipStream_t)stream);
+    return e == hipSuccess ? Q4_OK : device_error(e);
+}
+
+const char* q4g128_status_string(q4_status status) {
+    switch (status) {
+        case Q4_OK: return "Q4_OK: success";
+        case Q4_EINVAL: return "Q4_EINVAL: null pointer, non-positive size, batch outside 1..16 or overlapping output";
+        case Q4_ESHAPE: return "Q4_ESHAPE: K must be a multiple of 128 in [128, 32768]; sizes must fit the kernels' index range";
+        case Q4_EALIGN: return "Q4_EALIGN: packed/codes/activations need 16-byte, scales/mins 2-byte, outputs 4-byte alignment";
+        case Q4_EDEVICE: return "Q4_EDEVICE: the HIP runtime reported an error (see q4g128_last_hip_error)";
+    }
+    return "unknown q4g128 status";
+}
+
+int32_t q4g128_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,366 @@
+// int4 group-128 GEMV and small-batch matmat kernels for gfx950.
+//
+// Work mapping (depends on K only, never on the batch size, so that every
+// batched output column repeats the batch-1 arithmetic bit for bit):
+//   C   = K / 32 chunks per row (a chunk = 16 packed bytes = 32 codes);
+//   LPR = lanes per row, the largest of 64, 32, 16, 8, 4 dividing C;
+//   CPL = C / LPR chunks per lane; lane j of a row owns chunks j + t*LPR.
+// A wave therefore covers RPW = 64 / LPR rows per "pass"; one load
+// instruction of a wave reads RPW contiguous segments of LPR * 16 bytes.
+// Per lane and chunk: exact codes via dequant_dword, fp32 dot with the
+// activations (chunk_dot), then  y += scale*dot + min*sum(x)  (group_update).
+// The LPR lane partials of a row are summed by a fixed butterfly.
+#include "q4_device.hpp"
+#include "launch.hpp"
+
+namespace q4 {
+
+// ---------------------------------------------------------------------------
+// Batch-1 kernel: the activation slice of each lane lives in registers for
+// the whole kernel (CPL <= 4), staged once per workgroup through LDS.
+// Persistent grid: every wave walks passes p, p + W, p + 2W, ... (W = waves
+// in the grid) with two passes of weights in flight; the first two passes
+// are requested before the activations are staged.
+// ---------------------------------------------------------------------------
+
+template <int CPL>
+struct PassLoad {
+    u4 q[CPL];
+    uint16_t s[CPL];
+    uint16_t m[CPL];
+};
+
+template <int LPR, int CPL>
+__device__ __forceinline__ void load_pass(PassLoad<CPL>& L, const uint8_t* __restrict__ packed,
+                                          const uint16_t* __restrict__ scales,
+                                          const uint16_t* __restrict__ mins, int rowc, int k, int j) {
+    const int G = k >> 7;
+    const u4* rp = reinterpret_cast<const u4*>(packed + (size_t)rowc * (size_t)(k >> 1)) + j;
+    const size_t g0 = (size_t)rowc * (size_t)G + (size_t)(j >> 2);
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+        L.q[t] = __builtin_nontemporal_load(rp + t * LPR);
+        L.s[t] = scales[g0 + t * (LPR / 4)];
+        L.m[t] = mins[g0 + t * (LPR / 4)];
+    }
+}
+
+template <int LPR, int CPL>
+__device__ __forceinline__ void compute_pass(const PassLoad<CPL>& L, const h2 (&xp)[CPL][16],
+                                             const float (&xs)[CPL], const DequantConsts& kc,
+                                             float* __restrict__ y, int row, int n, int j) {
+    float yl = 0.0f;
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+        h2 codes[16];
+        dequant_dword(L.q[t].x, kc, codes + 0);
+        dequant_dword(L.q[t].y, kc, codes + 4);
+        dequant_dword(L.q[t].z, kc, codes + 8);
+        dequant_dword(L.q[t].w, kc, codes + 12);
+        const float dot = chunk_dot(codes, xp[t]);
+        yl = group_update(yl, L.s[t], L.m[t], dot, xs[t]);
+    }
+    yl = reduce_lanes<LPR>(yl);
+    if (j == 0 && row < n) y[row] = yl;
+}
+
+template <int LPR, int CPL>
+__global__ void __launch_bounds__(256)
+gemv_reg_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
+                const uint16_t* __restrict__ mins, const uint16_t* __restrict__ x,
+                float* __restrict__ y, int n, int k) {
+    constexpr int RPW = 64 / LPR;
+    extern __shared__ u4 x_lds[];  // [4][C]: quad d of chunk c at d*C + c, permuted pairs
+    const int C = k >> 5;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int j = lane % LPR;
+    const int rsub = lane / LPR;
+    const long passes = ((long)n + RPW - 1) / RPW;
+    const long W = (long)gridDim.x * (blockDim.x >> 6);
+    // Wave-major numbering: the passes of the last, partial round land on
+    // one wave of many different workgroups rather than on a few workgroups.
+    long p = (long)wave * gridDim.x + blockIdx.x;
+    auto row_of = [&](long pp) { return (int)(pp * RPW) + rsub; };
+    auto clamp = [&](int r) { return r < n ? r : n - 1; };
+
+    PassLoad<CPL> A, B;
+    if (p < passes) load_pass<LPR, CPL>(A, packed, scales, mins, clamp(row_of(p)), k, j);
+    if (p + W < passes) load_pass<LPR, CPL>(B, packed, scales, mins, clamp(row_of(p + W)), k, j);
+
+    // Stage x: window w (8 halves) = quad (w & 3) of chunk (w >> 2).
+    const u4* xv = reinterpret_cast<const u4*>(x);
+    for (int w = tid; w < (k >> 3); w += blockDim.x)
+        x_lds[(w & 3) * C + (w >> 2)] = permute_window(xv[w]);
+    __syncthreads();
+
+    h2 xp[CPL][16];
+    float xs[CPL];
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+        const int c = j + t * LPR;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const u4 v = x_lds[d * C + c];
+            xp[t][4 * d + 0] = as_h2(v.x);
+            xp[t][4 * d + 1] = as_h2(v.y);
+            xp[t][4 * d + 2] = as_h2(v.z);
+            xp[t][4 * d + 3] = as_h2(v.w);
+        }
+        xs[t] = chunk_xsum(xp[t]);
+    }
+    const DequantConsts kc = make_dequant_consts();
+
+    while (p < passes) {
+        compute_pass<LPR, CPL>(A, xp, xs, kc, y, row_of(p), n, j);
+        if (p + 2 * W < passes) load_pass<LPR, CPL>(A, packed, scales, mins, clamp(row_of(p + 2 * W)), k, j);
+        p += W;
+        if (p >= passes) break;
+        compute_pass<LPR, CPL>(B, xp, xs, kc, y, row_of(p), n, j);
+        if (p + 2 * W < passes) load_pass<LPR, CPL>(B, packed, scales, mins, clamp(row_of(p + 2 * W)), k, j);
+        p += W;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Batched kernel (also the batch-1 path when CPL > 4): BT activation columns
+// staged in LDS in permuted order with their per-chunk sums; the chunk loop
+// runs over t at run time.  Columns b >= nb are zero and never stored.
+// ---------------------------------------------------------------------------
+
+template <int LPR, int BT>
+__global__ void __launch_bounds__(512)
+gemm_batched_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
+                    const uint16_t* __restrict__ mins, const uint16_t* __restrict__ X,
+                    float* __restrict__ Y, int n, int k, int nb, int ppw) {
+    constexpr int RPW = 64 / LPR;
+    extern __shared__ u4 lds[];
+    const int C = k >> 5;
+    const int G = k >> 7;
+    u4* xq = lds;                                           // [BT][4][C]
+    float* xsum = reinterpret_cast<float*>(lds + (size_t)BT * 4 * C);  // [BT][C]
+    const int tid = threadIdx.x;
+
+    const int wpc = k >> 3;  // windows per column
+    for (int w = tid; w < BT * wpc; w += blockDim.x) {
+        const int b = w / wpc;
+        const int win = w - b * wpc;
+        u4 v = {0u, 0u, 0u, 0u};
+        if (b < nb) v = reinterpret_cast<const u4*>(X + (size_t)b * (size_t)k)[win];
+        xq[((size_t)b * 4 + (win & 3)) * C + (win >> 2)] = permute_window(v);
+    }
+    __syncthreads();
+    for (int w = tid; w < BT * C; w += blockDim.x) {
+        const int b = w / C;
+        const int c = w - b * C;
+        h2 xp[16];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const u4 v = xq[((size_t)b * 4 + d) * C + c];
+            xp[4 * d + 0] = as_h2(v.x);
+            xp[4 * d + 1] = as_h2(v.y);
+            xp[4 * d + 2] = as_h2(v.z);
+            xp[4 * d + 3] = as_h2(v.w);
+        }
+        xsum[w] = chunk_xsum(xp);
+    }
+    __syncthreads();
+
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int j = lane % LPR;
+    const int rsub = lane / LPR;
+    const int CPL = C / LPR;
+    const DequantConsts kc = make_dequant_consts();
+    const long passes = ((long)n + RPW - 1) / RPW;
+    const long p0 = ((long)blockIdx.x * (blockDim.x >> 6) + wave) * (long)ppw;
+
+    for (int i = 0; i < ppw; ++i) {
+        const long p = p0 + i;
+        if (p >= passes) break;
+        const int row = (int)(p * RPW) + rsub;
+        const int rowc = row < n ? row : n - 1;
+        const u4* rp = reinterpret_cast<const u4*>(packed + (size_t)rowc * (size_t)(k >> 1));
+        const size_t gbase = (size_t)rowc * (size_t)G;
+        float yl[BT];
+#pragma unroll
+        for (int b = 0; b < BT; ++b) yl[b] = 0.0f;
+        for (int t = 0; t < CPL; ++t) {
+            const int c = j + t * LPR;
+            const u4 q = __builtin_nontemporal_load(rp + c);
+            const uint16_t s = scales[gbase + (c >> 2)];
+            const uint16_t m = mins[gbase + (c >> 2)];
+            h2 codes[16];
+            dequant_dword(q.x, kc, codes + 0);
+            dequant_dword(q.y, kc, codes + 4);
+            dequant_dword(q.z, kc, codes + 8);
+            dequant_dword(q.w, kc, codes + 12);
+#pragma unroll
+            for (int b = 0; b < BT; ++b) {
+                h2 xp[16];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const u4 v = xq[((size_t)b * 4 + d) * C + c];
+                    xp[4 * d + 0] = as_h2(v.x);
+                    xp[4 * d + 1] = as_h2(v.y);
+                    xp[4 * d + 2] = as_h2(v.z);
+                    xp[4 * d + 3] = as_h2(v.w);
+                }
+                const float dot = chunk_dot(codes, xp);
+                yl[b] = group_update(yl[b], s, m, dot, xsum[b * C + c]);
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+            const float v = reduce_lanes<LPR>(yl[b]);
+            if (j == 0 && row < n && b < nb) Y[(size_t)b * (size_t)n + row] = v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers
+// ---------------------------------------------------------------------------
+
+int lanes_per_row(int k) {
+    const int C = k >> 5;
+    if (C % 64 == 0) return 64;
+    if (C % 32 == 0) return 32;
+    if (C % 16 == 0) return 16;
+    if (C % 8 == 0) return 8;
+    return 4;  // C = 4 * (K / 128) is always a multiple of 4
+}
+
+template <int LPR, int CPL>
+static hipError_t launch_reg(const GemvArgs& a, const DeviceInfo& dev, hipStream_t st) {
+    constexpr int RPW = 64 / LPR;
+    constexpr int kThreads = 256;
+    const size_t lds = (size_t)a.k * 2;
+    // Resident workgroups per CU for this instantiation (registers bound it;
+    // the LDS footprint is at most 16 KB).  Queried once per process.
+    static int per_cu = 0;
+    if (per_cu == 0) {
+        int nb = 0;
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &nb, reinterpret_cast<const void*>(&gemv_reg_kernel<LPR, CPL>), kThreads, 8192 * 2);
+        if (e != hipSuccess) return e;
+        per_cu = nb > 0 ? nb : 1;
+    }
+    const long passes = ((long)a.n + RPW - 1) / RPW;
+    long grid = (long)dev.num_cu * per_cu;
+    const long need = (passes + (kThreads / 64) - 1) / (kThreads / 64);
+    if (grid > need) grid = need;
+    hipLaunchKernelGGL((gemv_reg_kernel<LPR, CPL>), dim3((unsigned)grid), dim3(kThreads), lds, st,
+                       a.packed, a.scales, a.mins, a.x, a.y, a.n, a.k);
+    return hipGetLastError();
+}
+
+// Returns hipErrorNotSupported when (LPR, CPL) has no register-resident
+// instantiation; the caller then uses the batched kernel with one column.
+static hipError_t dispatch_reg(int lpr, int cpl, const GemvArgs& a, const DeviceInfo& dev, hipStream_t st) {
+#define Q4_REG(L, P) \
+    if (lpr == L && cpl == P) return launch_reg<L, P>(a, dev, st);
+    Q4_REG(64, 1) Q4_REG(64, 2) Q4_REG(64, 3) Q4_REG(64, 4)
+    Q4_REG(32, 1) Q4_REG(32, 3)
+    Q4_REG(16, 1) Q4_REG(16, 3)
+    Q4_REG(8, 1) Q4_REG(8, 3)
+    Q4_REG(4, 1) Q4_REG(4, 3)
+#undef Q4_REG
+    return hipErrorNotSupported;
+}
+
+template <int LPR, int BT>
+static hipError_t launch_batched(const GemvArgs& a, const uint16_t* X, float* Y, int nb,
+                                 const DeviceInfo& dev, hipStream_t st) {
+    constexpr int RPW = 64 / LPR;
+    const int C = a.k >> 5;
+    const size_t lds = (size_t)BT * 4 * C * 16 + (size_t)BT * C * 4;
+    static bool attr_set = false;  // per-process; the limit is the same on every gfx950 device
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_batched_kernel<LPR, BT>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)dev.max_lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const long passes = ((long)a.n + RPW - 1) / RPW;
+    const int waves = 8;
+    const long per_cu = lds <= dev.max_lds / 2 ? 2 : 1;
+    long grid = (long)dev.num_cu * per_cu;
+    const long need = (passes + waves - 1) / waves;
+    if (grid > need) grid = need;
+    const long ppw = (passes + grid * waves - 1) / (grid * waves);
+    grid = (passes + waves * ppw - 1) / (waves * ppw);
+    hipLaunchKernelGGL((gemm_batched_kernel<LPR, BT>), dim3((unsigned)grid), dim3(64 * waves), lds, st,
+                       a.packed, a.scales, a.mins, X, Y, a.n, a.k, nb, (int)ppw);
+    return hipGetLastError();
+}
+
+template <int LPR>
+static hipError_t dispatch_bt(int bt, const GemvArgs& a, const uint16_t* X, float* Y, int nb,
+                              const DeviceInfo& dev, hipStream_t st) {
+    switch (bt) {
+        case 1: return launch_batched<LPR, 1>(a, X, Y, nb, dev, st);
+        case 2: return launch_batched<LPR, 2>(a, X, Y, nb, dev, st);
+        case 4: return launch_batched<LPR, 4>(a, X, Y, nb, dev, st);
+        case 8: return launch_batched<LPR, 8>(a, X, Y, nb, dev, st);
+        case 16: return launch_batched<LPR, 16>(a, X, Y, nb, dev, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+static hipError_t dispatch_batched(int lpr, int bt, const GemvArgs& a, const uint16_t* X, float* Y,
+                                   int nb, const DeviceInfo& dev, hipStream_t st) {
+    switch (lpr) {
+        case 64: return dispatch_bt<64>(bt, a, X, Y, nb, dev, st);
+        case 32: return dispatch_bt<32>(bt, a, X, Y, nb, dev, st);
+        case 16: return dispatch_bt<16>(bt, a, X, Y, nb, dev, st);
+        case 8: return dispatch_bt<8>(bt, a, X, Y, nb, dev, st);
+        case 4: return dispatch_bt<4>(bt, a, X, Y, nb, dev, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+static int round_up_pow2_batch(int b) {
+    int bt = 1;
+    while (bt < b) bt <<= 1;
+    return bt;
+}
+
+// Largest column count per launch whose staged activations fit in LDS.
+static int max_cols_per_launch(int k, const DeviceInfo& dev) {
+    const size_t per_col = (size_t)k * 2 + (size_t)(k >> 5) * 4;
+    int cols = 16;
+    while (cols > 1 && (size_t)cols * per_col > dev.max_lds) cols >>= 1;
+    return cols;
+}
+
+hipError_t launch_gemv(const GemvArgs& a, const DeviceInfo& dev, hipStream_t st) {
+    const int lpr = lanes_per_row(a.k);
+    const int cpl = (a.k >> 5) / lpr;
+    hipError_t e = dispatch_reg(lpr, cpl, a, dev, st);
+    if (e != hipErrorNotSupported) return e;
+    return dispatch_batched(lpr, 1, a, a.x, a.y, 1, dev, st);
+}
+
+hipError_t launch_small_batch(const GemvArgs& a, const uint16_t* X, float* Y, int b,
+                              const DeviceInfo& dev, hipStream_t st) {
+    if (b == 1) {
+        GemvArgs one = a;
+        one.x = X;
+        one.y = Y;
+        return launch_gemv(one, dev, st);
+    }
+    const int lpr = lanes_per_row(a.k);
+    const int cap = max_cols_per_launch(a.k, dev);
+    for (int b0 = 0; b0 < b; b0 += cap) {
+        const int nb = (b - b0) < cap ? (b - b0) : cap;
+        const int bt = round_up_pow2_batch(nb);
+        hipError_t e = dispatch_batched(lpr, bt, a, X + (size_t)b0 * (size_t)a.k,
+                                        Y + (size_t)b0 * (size_t)a.n, nb, dev, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace q4

@@ -1,0 +1,37 @@
+// Internal host-side interface between the C-ABI layer (api.cpp) and the
+// kernel translation units.  Arguments reaching these launchers have already
+// been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q4 {
+
+struct DeviceInfo {
+    int device = -1;
+    int num_cu = 0;
+    size_t max_lds = 0;  // usable dynamic LDS bytes per workgroup
+};
+
+struct GemvArgs {
+    const uint8_t* packed;
+    const uint16_t* scales;
+    const uint16_t* mins;
+    const uint16_t* x;
+    float* y;
+    int n;
+    int k;
+};
+
+int lanes_per_row(int k);
+
+hipError_t launch_pack(const uint8_t* codes, uint8_t* packed, int64_t n, int64_t k, hipStream_t st);
+hipError_t launch_gemv(const GemvArgs& a, const DeviceInfo& dev, hipStream_t st);
+hipError_t launch_small_batch(const GemvArgs& a, const uint16_t* X, float* Y, int b,
+                              const DeviceInfo& dev, hipStream_t st);
+hipError_t launch_prefill(const GemvArgs& a, const uint16_t* X, float* Y, int m,
+                          const DeviceInfo& dev, hipStream_t st);
+
+}  // namespace q4

@@ -1,0 +1,137 @@
+// Device-side building blocks shared by the gfx950 kernels of the int4
+// group-128 library.  Everything here is per-lane arithmetic whose order is
+// fixed, so that every kernel that calls it produces the same bits for the
+// same (row, column) pair.
+//
+// Unit of work: a "chunk" is 16 bytes of one packed row = 32 consecutive
+// codes = a quarter of a 128-column group.  A chunk is consumed as four
+// dwords of eight codes each.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
+__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// Constants of the nibble -> fp16 conversion, materialised once per kernel.
+// gfx950 VOP3 instructions cannot encode literals and read at most one
+// scalar register, so the two masks live in SGPRs and the exponent pattern
+// in a VGPR; each nibble pair then costs a single v_and_or_b32.
+struct DequantConsts {
+    uint32_t mask_lo;  // 0x000F000F: nibbles 0 and 4 of a dword
+    uint32_t mask_hi;  // 0x00F000F0: nibbles 1 and 5 of a dword
+    uint32_t magic;    // 0x64006400: fp16 1024.0 in both halves
+};
+
+__device__ __forceinline__ DequantConsts make_dequant_consts() {
+    DequantConsts c;
+    asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(c.mask_lo));
+    asm volatile("s_mov_b32 %0, 0x00F000F0" : "=s"(c.mask_hi));
+    uint32_t m;
+    asm volatile("s_mov_b32 %0, 0x64006400" : "=s"(m));
+    asm volatile("v_mov_b32 %0, %1" : "=v"(c.magic) : "s"(m));
+    return c;
+}
+
+// Eight codes of one dword -> four fp16 pairs holding the EXACT codes.
+//
+// Byte b of the dword holds columns 2b (bits 0..3) and 2b+1 (bits 4..7).
+// OR-ing a nibble into the mantissa of fp16 1024.0 (exponent 10, so the
+// mantissa's unit is 1) gives 1024 + c with no integer-to-float convert;
+// a nibble in mantissa bits 4..7 gives 1024 + 16c.  The bias is then removed
+// exactly: (1024 + c) - 1024 = c, and (1024 + 16c) * (1/16) - 64 = c in one
+// fused multiply-add.  Output pair order (columns within the 8):
+//   out[0] = (c0, c4), out[1] = (c1, c5), out[2] = (c2, c6), out[3] = (c3, c7).
+__device__ __forceinline__ void dequant_dword(uint32_t q, const DequantConsts& k, h2 out[4]) {
+    const uint32_t q8 = q >> 8;
+    const uint32_t a = (q & k.mask_lo) | k.magic;
+    const uint32_t b = (q & k.mask_hi) | k.magic;
+    const uint32_t c = (q8 & k.mask_lo) | k.magic;
+    const uint32_t d = (q8 & k.mask_hi) | k.magic;
+    const h2 bias = {(_Float16)1024.0f, (_Float16)1024.0f};
+    const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h2 neg64 = {(_Float16)-64.0f, (_Float16)-64.0f};
+    out[0] = as_h2(a) - bias;
+    out[1] = __builtin_elementwise_fma(as_h2(b), sixteenth, neg64);
+    out[2] = as_h2(c) - bias;
+    out[3] = __builtin_elementwise_fma(as_h2(d), sixteenth, neg64);
+}
+
+// Eight consecutive fp16 activations (one 16-byte window, natural order
+// x0..x7) -> the pair order produced by dequant_dword:
+//   (x0, x4), (x1, x5), (x2, x6), (x3, x7).
+__device__ __forceinline__ u4 permute_window(u4 v) {
+    u4 r;
+    r.x = (v.x & 0xFFFFu) | (v.z << 16);
+    r.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+    r.z = (v.y & 0xFFFFu) | (v.w << 16);
+    r.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+    return r;
+}
+
+// Sum of the 32 activations of a chunk, from its 16 permuted pairs, in fp32
+// with a fixed order (pair 0 first).
+__device__ __forceinline__ float chunk_xsum(const h2 xp[16]) {
+    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc = __builtin_amdgcn_fdot2(xp[i], one, acc, false);
+    return acc;
+}
+
+// sum(code * x) over one chunk: codes and activations as 16 fp16 pairs in
+// matching order, exact products, fp32 accumulation starting from 0, pair 0
+// first.  Every kernel that needs this value calls this function (or
+// interleaves dequant_dword with the same sequence of dot steps).
+__device__ __forceinline__ float chunk_dot(const h2 codes[16], const h2 xp[16]) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc = __builtin_amdgcn_fdot2(codes[i], xp[i], acc, false);
+    return acc;
+}
+
+// One group-slice update of a lane's running row sum:
+//   y += scale * sum(code*x) ; y += min * sum(x)
+// i.e. sum((code*scale + min) * x) over the slice, with each term once.
+__device__ __forceinline__ float group_update(float y, uint16_t s_bits, uint16_t m_bits, float dot, float xsum) {
+    y = __builtin_fmaf(f16_bits_to_f32(s_bits), dot, y);
+    y = __builtin_fmaf(f16_bits_to_f32(m_bits), xsum, y);
+    return y;
+}
+
+// Butterfly sum over aligned groups of LPR lanes (LPR a power of two <= 64).
+// Pairing per level: lane i with i^1, then i^2, then the other half of its
+// 8-lane group (row_half_mirror), the other half of its 16-lane row
+// (row_mirror), the other row of its 32-lane half (ds_swizzle xor 16) and the
+// other half of the wave.  Each level pairs the same partial sums as an xor
+// butterfly, and every lane of a group ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+template <int LPR>
+__device__ __forceinline__ float reduce_lanes(float v) {
+    if constexpr (LPR >= 2) v = v + dpp_move<0xB1>(v);    // quad_perm [1,0,3,2]
+    if constexpr (LPR >= 4) v = v + dpp_move<0x4E>(v);    // quad_perm [2,3,0,1]
+    if constexpr (LPR >= 8) v = v + dpp_move<0x141>(v);   // row_half_mirror
+    if constexpr (LPR >= 16) v = v + dpp_move<0x140>(v);  // row_mirror
+    if constexpr (LPR >= 32)
+        v = v + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+    if constexpr (LPR >= 64) v = v + __shfl_xor(v, 32, 64);
+    return v;
+}
+
+}  // namespace q4

@@ -1,0 +1,122 @@
+"""C-ABI checks that run without a GPU.
+
+The library must load, export every entry point that include/q4g128.h
+declares, and reject every invalid argument combination with the documented
+status code BEFORE any HIP call.  Pointer arguments here are fake addresses
+that are never dereferenced: each call fails validation first.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4g128.h")
+
+q4 = pytest.importorskip("int4_group_quantized_amd")
+
+EINVAL, ESHAPE, EALIGN, OK = q4.Q4_EINVAL, q4.Q4_ESHAPE, q4.Q4_EALIGN, q4.Q4_OK
+
+A = 0x7F0000000000  # 256-byte aligned fake device addresses, far apart
+P, S, M, X, Y = (A + i * (1 << 36) for i in range(5))
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"Q4_API\s+[\w\s\*]+?\b(q4g128_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_symbols() == sorted(q4.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = q4.library()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    # the object file exports exactly these functions
+    out = os.popen(f"nm -D --defined-only {q4.LIB_PATH}").read()
+    funcs = sorted(line.split()[-1] for line in out.splitlines() if " T " in line)
+    assert funcs == declared_symbols()
+
+
+def test_status_strings():
+    for code in (OK, EINVAL, ESHAPE, EALIGN, q4.Q4_EDEVICE):
+        s = q4.q4g128_status_string(code)
+        assert s.startswith("Q4_"), s
+    assert "unknown" in q4.q4g128_status_string(-99)
+    assert q4.library().q4g128_last_hip_error() == 0
+
+
+def gemv(p=P, s=S, m=M, x=X, y=Y, n=64, k=256):
+    return q4.library().q4g128_gemv(p, s, m, x, y, n, k, None)
+
+
+def batch(b, p=P, s=S, m=M, x=X, y=Y, n=64, k=256):
+    return q4.library().q4g128_gemm_small_batch(p, s, m, x, y, n, k, b, None)
+
+
+def prefill(mm, p=P, s=S, m=M, x=X, y=Y, n=64, k=256):
+    return q4.library().q4g128_gemm_prefill(p, s, m, x, y, n, k, mm, None)
+
+
+def pack(c=X, p=P, n=64, k=256):
+    return q4.library().q4g128_pack(c, p, n, k, None)
+
+
+@pytest.mark.parametrize("call", [
+    lambda: gemv(p=None), lambda: gemv(s=None), lambda: gemv(m=None), lambda: gemv(x=None),
+    lambda: gemv(y=None), lambda: gemv(n=0), lambda: gemv(n=-5),
+    lambda: batch(0), lambda: batch(17), lambda: batch(-1), lambda: batch(4, x=None),
+    lambda: prefill(0), lambda: prefill(-3), lambda: prefill(34, y=None),
+    lambda: pack(c=None), lambda: pack(p=None), lambda: pack(n=0),
+])
+def test_einval(call):
+    assert call() == EINVAL
+
+
+@pytest.mark.parametrize("k", [0, 64, 127, 130, 200, 32768 + 128, -128])
+def test_eshape_k(k):
+    expect = ESHAPE
+    assert gemv(k=k) == expect
+    assert batch(3, k=k) == expect
+    assert prefill(5, k=k) == expect
+    assert pack(k=k) == expect
+
+
+def test_eshape_sizes():
+    assert gemv(n=1 << 31) == ESHAPE
+    assert prefill(1 << 31) == ESHAPE
+
+
+@pytest.mark.parametrize("which", ["p", "x", "s", "m", "y"])
+def test_ealign(which):
+    bad = {"p": P + 8, "x": X + 4, "s": S + 1, "m": M + 1, "y": Y + 2}[which]
+    assert gemv(**{which: bad}) == EALIGN
+    assert batch(2, **{which: bad}) == EALIGN
+    assert prefill(20, **{which: bad}) == EALIGN
+
+
+def test_alignment_minimums_accepted_by_validation_order():
+    # 2-byte aligned scales pass the alignment check and fail on something
+    # else we planted (n = 0), proving the documented minimum is 2 bytes.
+    assert gemv(s=S + 2, n=0) == EINVAL
+    assert pack(c=X + 8) == EALIGN
+    assert pack(p=P + 1) == EALIGN
+
+
+def test_overlapping_output_rejected():
+    # y inside the packed weights, inside x, inside scales
+    assert gemv(y=P + 64) == EINVAL
+    assert gemv(y=X) == EINVAL
+    assert batch(4, y=S + 16) == EINVAL
+    assert prefill(8, y=M) == EINVAL
+    assert pack(p=X + 16) == EINVAL  # packed overlaps codes
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    codes = torch.zeros((4, 128), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        q4.q4g128_pack(codes)

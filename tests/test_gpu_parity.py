@@ -1,0 +1,231 @@
+"""GPU parity: the HIP library against the fp64 CPU oracle.
+
+Every call goes through the C ABI (via the thin ctypes binding).  Inputs are
+seeded synthetic draws from synth/; expected values come from oracle/ or from
+the hand-derived known answers in tests/golden/.
+"""
+import numpy as np
+import pytest
+
+import golden_cases
+import oracle
+import synth
+from gpu_helpers import (assert_bound, assert_rel, cpu, device, gemv_bound, note, prefill_bound_T,
+                         to_dev_f16, upload)
+from test_oracle_pins import dyadic_case
+
+pytestmark = pytest.mark.gpu
+
+q4 = pytest.importorskip("int4_group_quantized_amd")
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    note(f"[gpu-test] {request.node.nodeid}")
+    yield
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+# --------------------------------------------------------------------------
+# pack
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,k,seed", [(1, 128, 0), (3, 256, 1), (256, 512, 2), (77, 3072, 3), (5, 32768, 4)])
+def test_pack_bit_exact(dev, n, k, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    codes = rng.integers(0, 256, (n, k), dtype=np.uint8)  # high bits must be ignored
+    got = cpu(q4.q4g128_pack(torch.from_numpy(codes).to(dev)))
+    assert np.array_equal(got, oracle.pack(codes))
+
+
+def test_pack_full_size(dev):
+    w = synth.weights(synth.FUSED_N, synth.HIDDEN_K, synth.SEEDS["fused"])
+    got = cpu(q4.q4g128_pack(torch.from_numpy(w.codes).to(dev)))
+    assert np.array_equal(got, oracle.pack(w.codes))
+
+
+# --------------------------------------------------------------------------
+# known answers and exact dyadic cases: bit-exact
+# --------------------------------------------------------------------------
+
+def _golden_on_gpu(case, dev):
+    if case.packed is not None:
+        packed = torch.from_numpy(case.packed).to(dev)
+    else:
+        packed = q4.q4g128_pack(torch.from_numpy(case.codes).to(dev))
+    return packed, to_dev_f16(case.scales, dev), to_dev_f16(case.mins, dev), to_dev_f16(case.x, dev)
+
+
+@pytest.mark.parametrize("case", golden_cases.load(), ids=lambda c: c.name)
+def test_known_answers_exact(dev, case):
+    packed, s, m, x = _golden_on_gpu(case, dev)
+    assert float(cpu(q4.q4g128_gemv(packed, s, m, x))[0]) == case.expected
+    X = x.reshape(1, -1).repeat(3, 1).contiguous()
+    assert np.all(cpu(q4.q4g128_gemm_small_batch(packed, s, m, X)) == case.expected)
+    assert np.all(cpu(q4.q4g128_gemm_prefill(packed, s, m, X)) == case.expected)
+
+
+@pytest.mark.parametrize("n,k", [(4, 384), (37, 3072), (9, 8192), (130, 512), (3, 11008), (2, 32768)])
+def test_dyadic_bit_exact(dev, n, k):
+    for seed in range(2):
+        _, _, codes, scales, mins, x = dyadic_case(seed, n, k)
+        ref = oracle.gemv(oracle.pack(codes), scales, mins, x)
+        w = synth.Weights(codes, scales, mins)
+        packed, s, m = upload(w, dev, q4)
+        xd = to_dev_f16(x, dev)
+        assert np.array_equal(cpu(q4.q4g128_gemv(packed, s, m, xd)).astype(np.float64), ref)
+        X = xd.reshape(1, -1).repeat(5, 1).contiguous()
+        Yb = cpu(q4.q4g128_gemm_small_batch(packed, s, m, X)).astype(np.float64)
+        assert np.array_equal(Yb, np.tile(ref, (5, 1)))
+        Yp = cpu(q4.q4g128_gemm_prefill(packed, s, m, X)).astype(np.float64)
+        assert np.array_equal(Yp, np.tile(ref, (5, 1)))
+
+
+# --------------------------------------------------------------------------
+# random parity at tolerance (every lanes-per-row / chunks-per-lane variant)
+# --------------------------------------------------------------------------
+
+SHAPES = [
+    (1, 128), (2, 256), (3, 384), (17, 512), (33, 640), (255, 768), (64, 1024), (5, 1152),
+    (1000, 2048), (129, 3072), (31, 4096), (7, 6144), (300, 8192), (19, 11008), (3, 16384), (2, 32768),
+]
+
+
+@pytest.mark.parametrize("n,k", SHAPES)
+def test_gemv_parity_shapes(dev, n, k):
+    w, x = synth.gemv_case(n, k, seed=n * 7919 + k)
+    packed_np = oracle.pack(w.codes)
+    packed, s, m = upload(w, dev, q4)
+    y = cpu(q4.q4g128_gemv(packed, s, m, to_dev_f16(x[0], dev)))
+    ref = oracle.gemv(packed_np, w.scales, w.mins, x[0])
+    assert_rel(y, ref, f"gemv {n}x{k}")
+    assert_bound(y, ref, gemv_bound(packed_np, w, x)[0], 128, f"gemv {n}x{k}")
+
+
+@pytest.mark.parametrize("name", ["tiny_256x512", "fused_25088x3072", "oproj_3072x3072", "down_3072x8192"])
+def test_gemv_parity_workloads(dev, name):
+    w, x = synth.workload(name)
+    packed_np = oracle.pack(w.codes)
+    packed, s, m = upload(w, dev, q4)
+    assert np.array_equal(cpu(packed), packed_np)
+    y = cpu(q4.q4g128_gemv(packed, s, m, to_dev_f16(x[0], dev)))
+    ref = oracle.gemv(packed_np, w.scales, w.mins, x[0])
+    assert_rel(y, ref, name)
+    assert_bound(y, ref, gemv_bound(packed_np, w, x)[0], 128, name)
+
+
+def test_gemv_zero_and_scaling(dev):
+    w, x = synth.gemv_case(96, 3072, seed=42)
+    packed, s, m = upload(w, dev, q4)
+    zero = torch.zeros(3072, dtype=torch.float16, device=dev)
+    assert np.all(cpu(q4.q4g128_gemv(packed, s, m, zero)) == 0)
+    y1 = cpu(q4.q4g128_gemv(packed, s, m, to_dev_f16(x[0], dev)))
+    y4 = cpu(q4.q4g128_gemv(packed, s, m, to_dev_f16((x[0].astype(np.float64) * 4).astype(np.float16), dev)))
+    assert np.array_equal(y4, y1 * 4)  # power-of-two scaling is exact in every rounding step
+
+
+# --------------------------------------------------------------------------
+# batch: bit-identity with the batch-1 call, and parity
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,k", [(25088, 3072), (3072, 8192), (257, 512), (100, 11008), (33, 384), (9, 32768)])
+def test_small_batch_bit_identical_to_gemv(dev, n, k):
+    w = synth.weights(n, k, seed=n + k)
+    packed, s, m = upload(w, dev, q4)
+    X = synth.activations(16, k, seed=4)
+    Xd = to_dev_f16(X, dev)
+    singles = np.stack([cpu(q4.q4g128_gemv(packed, s, m, Xd[b].contiguous())) for b in range(16)])
+    for b in range(1, 17):
+        Y = cpu(q4.q4g128_gemm_small_batch(packed, s, m, Xd[:b].contiguous()))
+        assert np.array_equal(Y, singles[:b]), f"B={b}: batched rows differ from the batch-1 call"
+
+
+@pytest.mark.parametrize("b", [2, 4, 8, 16])
+def test_small_batch_parity_fused(dev, b):
+    w = synth.weights(synth.FUSED_N, synth.HIDDEN_K, synth.SEEDS["fused"])
+    X = synth.batch_activations(b)
+    packed_np = oracle.pack(w.codes)
+    packed, s, m = upload(w, dev, q4)
+    Y = cpu(q4.q4g128_gemm_small_batch(packed, s, m, to_dev_f16(X, dev)))
+    ref = oracle.gemm(packed_np, w.scales, w.mins, X)
+    assert_rel(Y, ref, f"batch B={b}")
+    assert_bound(Y, ref, oracle.term_magnitude(packed_np, w.scales, w.mins, X), 128, f"batch B={b}")
+
+
+def test_determinism_and_row_permutation(dev):
+    w, x = synth.gemv_case(4099, 3072, seed=77)
+    packed, s, m = upload(w, dev, q4)
+    xd = to_dev_f16(x[0], dev)
+    y0 = cpu(q4.q4g128_gemv(packed, s, m, xd))
+    for _ in range(3):
+        assert np.array_equal(cpu(q4.q4g128_gemv(packed, s, m, xd)), y0)
+    perm = np.random.Generator(np.random.PCG64(3)).permutation(4099)
+    wp = synth.Weights(w.codes[perm], w.scales[perm], w.mins[perm])
+    pp, sp, mp = upload(wp, dev, q4)
+    assert np.array_equal(cpu(q4.q4g128_gemv(pp, sp, mp, xd)), y0[perm])
+
+
+def test_non_default_stream(dev):
+    w, x = synth.gemv_case(512, 1024, seed=5)
+    packed, s, m = upload(w, dev, q4)
+    xd = to_dev_f16(x[0], dev)
+    ref = cpu(q4.q4g128_gemv(packed, s, m, xd))
+    st = torch.cuda.Stream(dev)
+    with torch.cuda.stream(st):
+        y = q4.q4g128_gemv(packed, s, m, xd, stream=st)
+    st.synchronize()
+    assert np.array_equal(y.cpu().numpy(), ref)
+
+
+# --------------------------------------------------------------------------
+# prompt processing (matrix cores, fp16 weights)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mtok,n,k", [(1, 64, 128), (2, 70, 384), (15, 100, 512), (16, 128, 3072), (17, 65, 3072),
+                                      (34, 200, 3072), (100, 33, 8192), (112, 128, 1024), (300, 64, 2048),
+                                      (5, 40, 32768)])
+def test_prefill_parity_shapes(dev, mtok, n, k):
+    w = synth.weights(n, k, seed=mtok * 1000 + n)
+    X = synth.activations(mtok, k, seed=mtok + 17)
+    packed_np = oracle.pack(w.codes)
+    packed, s, m = upload(w, dev, q4)
+    Y = cpu(q4.q4g128_gemm_prefill(packed, s, m, to_dev_f16(X, dev)))
+    assert_rel(Y, oracle.gemm(packed_np, w.scales, w.mins, X), f"prefill M={mtok} {n}x{k}")
+    assert_bound(Y, oracle.gemm_fp16_weights(packed_np, w.scales, w.mins, X),
+                 prefill_bound_T(packed_np, w, X), 256, f"prefill fp16-w M={mtok}")
+
+
+@pytest.mark.parametrize("mtok", [34, 256])
+def test_prefill_parity_fused(dev, mtok):
+    w = synth.weights(synth.FUSED_N, synth.HIDDEN_K, synth.SEEDS["fused"])
+    X = synth.prefill_activations(mtok)
+    packed_np = oracle.pack(w.codes)
+    packed, s, m = upload(w, dev, q4)
+    Y = cpu(q4.q4g128_gemm_prefill(packed, s, m, to_dev_f16(X, dev)))
+    assert_rel(Y, oracle.gemm(packed_np, w.scales, w.mins, X), f"prefill M={mtok}")
+    assert_bound(Y, oracle.gemm_fp16_weights(packed_np, w.scales, w.mins, X),
+                 prefill_bound_T(packed_np, w, X), 256, f"prefill fp16-w M={mtok}")
+
+
+# --------------------------------------------------------------------------
+# the 36-layer decode stack: sampled layers at full size, launched back to
+# back on one stream as the benchmark does
+# --------------------------------------------------------------------------
+
+def test_stack_sampled_layers(dev):
+    shapes = [(synth.FUSED_N, synth.HIDDEN_K), (synth.OPROJ_N, synth.OPROJ_K), (synth.DOWN_N, synth.DOWN_K)]
+    for layer in (0, 35):
+        mats = []
+        for which, (n, k) in enumerate(shapes):
+            w = synth.weights(n, k, synth.stack_seed(layer, which))
+            mats.append((w, upload(w, dev, q4)))
+        xs = [synth.activations(1, k, seed=90000 + layer * 3 + i)[0] for i, (_, k) in enumerate(shapes)]
+        outs = [q4.q4g128_gemv(p, s, m, to_dev_f16(x, dev)) for (w, (p, s, m)), x in zip(mats, xs)]
+        for (w, _), x, y in zip(mats, xs, outs):
+            ref = oracle.gemv(oracle.pack(w.codes), w.scales, w.mins, x)
+            assert_rel(cpu(y), ref, f"stack layer {layer} {w.n}x{w.k}")
