@@ -7,9 +7,11 @@
 //   CPL = C / LPR chunks per lane; lane j of a row owns chunks j + t*LPR.
 // A wave therefore covers RPW = 64 / LPR rows per "pass"; one load
 // instruction of a wave reads RPW contiguous segments of LPR * 16 bytes.
-// Per lane and chunk: exact codes via dequant_dword, fp32 dot with the
-// activations (chunk_dot), then  y += scale*dot + min*sum(x)  (group_update).
-// The LPR lane partials of a row are summed by a fixed butterfly.
+// Per lane and chunk: codes as exact fp16 denormals (chunk_codes), exact
+// products with the activations accumulated in fp32 (chunk_dot), then
+//   y += scale * dot + min * sum(x)   (group_update),
+// all carried in units of 2^-20.  The LPR lane partials of a row are summed
+// by a fixed butterfly and the row sum is rescaled by 2^20 (exact).
 #include "q4_device.hpp"
 #include "launch.hpp"
 
@@ -47,20 +49,17 @@ __device__ __forceinline__ void load_pass(PassLoad<CPL>& L, const uint8_t* __res
 
 template <int LPR, int CPL>
 __device__ __forceinline__ void compute_pass(const PassLoad<CPL>& L, const h2 (&xp)[CPL][16],
-                                             const float (&xs)[CPL], const DequantConsts& kc,
-                                             float* __restrict__ y, int row, int n, int j) {
+                                             const float (&xs)[CPL], float* __restrict__ y, int row,
+                                             int n, int j) {
     float yl = 0.0f;
 #pragma unroll
     for (int t = 0; t < CPL; ++t) {
         h2 codes[16];
-        dequant_dword(L.q[t].x, kc, codes + 0);
-        dequant_dword(L.q[t].y, kc, codes + 4);
-        dequant_dword(L.q[t].z, kc, codes + 8);
-        dequant_dword(L.q[t].w, kc, codes + 12);
+        chunk_codes(L.q[t], codes);
         const float dot = chunk_dot(codes, xp[t]);
         yl = group_update(yl, L.s[t], L.m[t], dot, xs[t]);
     }
-    yl = reduce_lanes<LPR>(yl);
+    yl = reduce_lanes<LPR>(yl) * kInvUnit;
     if (j == 0 && row < n) y[row] = yl;
 }
 
@@ -110,14 +109,13 @@ gemv_reg_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__
         }
         xs[t] = chunk_xsum(xp[t]);
     }
-    const DequantConsts kc = make_dequant_consts();
 
     while (p < passes) {
-        compute_pass<LPR, CPL>(A, xp, xs, kc, y, row_of(p), n, j);
+        compute_pass<LPR, CPL>(A, xp, xs, y, row_of(p), n, j);
         if (p + 2 * W < passes) load_pass<LPR, CPL>(A, packed, scales, mins, clamp(row_of(p + 2 * W)), k, j);
         p += W;
         if (p >= passes) break;
-        compute_pass<LPR, CPL>(B, xp, xs, kc, y, row_of(p), n, j);
+        compute_pass<LPR, CPL>(B, xp, xs, y, row_of(p), n, j);
         if (p + 2 * W < passes) load_pass<LPR, CPL>(B, packed, scales, mins, clamp(row_of(p + 2 * W)), k, j);
         p += W;
     }
@@ -172,7 +170,6 @@ gemm_batched_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
     const int j = lane % LPR;
     const int rsub = lane / LPR;
     const int CPL = C / LPR;
-    const DequantConsts kc = make_dequant_consts();
     const long passes = ((long)n + RPW - 1) / RPW;
     const long p0 = ((long)blockIdx.x * (blockDim.x >> 6) + wave) * (long)ppw;
 
@@ -192,10 +189,7 @@ gemm_batched_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
             const uint16_t s = scales[gbase + (c >> 2)];
             const uint16_t m = mins[gbase + (c >> 2)];
             h2 codes[16];
-            dequant_dword(q.x, kc, codes + 0);
-            dequant_dword(q.y, kc, codes + 4);
-            dequant_dword(q.z, kc, codes + 8);
-            dequant_dword(q.w, kc, codes + 12);
+            chunk_codes(q, codes);
 #pragma unroll
             for (int b = 0; b < BT; ++b) {
                 h2 xp[16];
@@ -213,7 +207,7 @@ gemm_batched_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
         }
 #pragma unroll
         for (int b = 0; b < BT; ++b) {
-            const float v = reduce_lanes<LPR>(yl[b]);
+            const float v = reduce_lanes<LPR>(yl[b]) * kInvUnit;
             if (j == 0 && row < n && b < nb) Y[(size_t)b * (size_t)n + row] = v;
         }
     }

@@ -25,10 +25,93 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
     return (float)__builtin_bit_cast(_Float16, b);
 }
 
-// Constants of the nibble -> fp16 conversion, materialised once per kernel.
-// gfx950 VOP3 instructions cannot encode literals and read at most one
-// scalar register, so the two masks live in SGPRs and the exponent pattern
-// in a VGPR; each nibble pair then costs a single v_and_or_b32.
+// ---------------------------------------------------------------------------
+// Matrix-vector path: codes as fp16 denormals.
+//
+// An fp16 whose exponent field is zero is a denormal worth mantissa * 2^-24,
+// with no implicit leading one.  Masking a dword of packed codes therefore
+// yields exact, bias-free fp16 pairs in one AND each:
+//   q        & 0x000F000F -> (c0, c4) * 2^-24     (nibbles in bits 0..3)
+//   q        & 0x00F000F0 -> (c1, c5) * 2^-20     (nibbles in bits 4..7)
+//   (q >> 8) & 0x000F000F -> (c2, c6) * 2^-24
+//   (q >> 8) & 0x00F000F0 -> (c3, c7) * 2^-20
+// (byte b of the dword holds columns 2b and 2b+1 in its low and high
+// nibble).  v_dot2_f32_f16 multiplies these by the fp16 activations
+// exactly, so the products carry the scale 2^-24 or 2^-20; the two scales
+// are summed in separate fp32 chains (lo = L * 2^-24, hi = H * 2^-20) and
+// joined exactly as lo * 16 + hi = (L + H) * 2^-20.  One chunk costs 1 shift + 4 ANDs + 4 dot2 per 8 codes.
+// ---------------------------------------------------------------------------
+
+constexpr float kLoScale = 16.0f;          // (L * 2^-24) * 16 = L * 2^-20
+constexpr float kUnit = 9.5367431640625e-07f;  // 2^-20: scale of chunk dots and sums
+constexpr float kInvUnit = 1048576.0f;    // 2^20
+
+// 32 codes of a chunk -> 16 fp16 pairs (see above) in pair order
+//   [4d + 0] = (c0, c4), [4d + 1] = (c1, c5), [4d + 2] = (c2, c6), [4d + 3] = (c3, c7)
+// for dword d of the chunk (columns 8d .. 8d+7).
+__device__ __forceinline__ void chunk_codes(const u4 q, h2 codes[16]) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t q8 = w[d] >> 8;
+        codes[4 * d + 0] = as_h2(w[d] & 0x000F000Fu);
+        codes[4 * d + 1] = as_h2(w[d] & 0x00F000F0u);
+        codes[4 * d + 2] = as_h2(q8 & 0x000F000Fu);
+        codes[4 * d + 3] = as_h2(q8 & 0x00F000F0u);
+    }
+}
+
+// sum(code * x) * 2^-20 over one chunk, from chunk_codes() and the 16
+// activation pairs in the same order.  Exact products; two fp32 chains
+// starting from 0 (pairs 0, 2, 4, ... and 1, 3, 5, ...), then
+// lo * 16 + hi in one fused multiply-add (the multiply is exact).  Every kernel that needs a chunk dot calls this.
+__device__ __forceinline__ float chunk_dot(const h2 codes[16], const h2 xp[16]) {
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+        lo = __builtin_amdgcn_fdot2(codes[i], xp[i], lo, false);
+        hi = __builtin_amdgcn_fdot2(codes[i + 1], xp[i + 1], hi, false);
+    }
+    return __builtin_fmaf(lo, kLoScale, hi);
+}
+
+// Eight consecutive fp16 activations (one 16-byte window, natural order
+// x0..x7) -> the pair order of the code pairs:
+//   (x0, x4), (x1, x5), (x2, x6), (x3, x7).
+__device__ __forceinline__ u4 permute_window(u4 v) {
+    u4 r;
+    r.x = (v.x & 0xFFFFu) | (v.z << 16);
+    r.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+    r.z = (v.y & 0xFFFFu) | (v.w << 16);
+    r.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+    return r;
+}
+
+// sum(x) * 2^-20 over the 32 activations of a chunk, from its 16 permuted
+// pairs, in fp32 with a fixed order (pair 0 first).
+__device__ __forceinline__ float chunk_xsum(const h2 xp[16]) {
+    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc = __builtin_amdgcn_fdot2(xp[i], one, acc, false);
+    return acc * kUnit;
+}
+
+// ---------------------------------------------------------------------------
+// Prompt-processing path: exact integer-valued fp16 codes.
+//
+// OR-ing a nibble into the mantissa of fp16 1024.0 (exponent 10, so the
+// mantissa's unit is 1) gives 1024 + c with no integer-to-float convert; a
+// nibble in mantissa bits 4..7 gives 1024 + 16c.  The bias is removed
+// exactly: (1024 + c) - 1024 = c and (1024 + 16c) * (1/16) - 64 = c.  The
+// result feeds fp16 arithmetic (w = fma(c, scale, min)), which needs the
+// code itself rather than a scaled denormal.
+// ---------------------------------------------------------------------------
+
+// Constants of that conversion, materialised once per kernel.  gfx950 VOP3
+// instructions cannot encode literals and read at most one scalar register,
+// so the masks live in SGPRs and the exponent pattern in a VGPR; each
+// nibble pair then costs a single v_and_or_b32.
 struct DequantConsts {
     uint32_t mask_lo;  // 0x000F000F: nibbles 0 and 4 of a dword
     uint32_t mask_hi;  // 0x00F000F0: nibbles 1 and 5 of a dword
@@ -45,15 +128,8 @@ __device__ __forceinline__ DequantConsts make_dequant_consts() {
     return c;
 }
 
-// Eight codes of one dword -> four fp16 pairs holding the EXACT codes.
-//
-// Byte b of the dword holds columns 2b (bits 0..3) and 2b+1 (bits 4..7).
-// OR-ing a nibble into the mantissa of fp16 1024.0 (exponent 10, so the
-// mantissa's unit is 1) gives 1024 + c with no integer-to-float convert;
-// a nibble in mantissa bits 4..7 gives 1024 + 16c.  The bias is then removed
-// exactly: (1024 + c) - 1024 = c, and (1024 + 16c) * (1/16) - 64 = c in one
-// fused multiply-add.  Output pair order (columns within the 8):
-//   out[0] = (c0, c4), out[1] = (c1, c5), out[2] = (c2, c6), out[3] = (c3, c7).
+// Eight codes of one dword -> four fp16 pairs holding the exact codes, in
+// the pair order (c0, c4), (c1, c5), (c2, c6), (c3, c7).
 __device__ __forceinline__ void dequant_dword(uint32_t q, const DequantConsts& k, h2 out[4]) {
     const uint32_t q8 = q >> 8;
     const uint32_t a = (q & k.mask_lo) | k.magic;
@@ -69,40 +145,7 @@ __device__ __forceinline__ void dequant_dword(uint32_t q, const DequantConsts& k
     out[3] = __builtin_elementwise_fma(as_h2(d), sixteenth, neg64);
 }
 
-// Eight consecutive fp16 activations (one 16-byte window, natural order
-// x0..x7) -> the pair order produced by dequant_dword:
-//   (x0, x4), (x1, x5), (x2, x6), (x3, x7).
-__device__ __forceinline__ u4 permute_window(u4 v) {
-    u4 r;
-    r.x = (v.x & 0xFFFFu) | (v.z << 16);
-    r.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
-    r.z = (v.y & 0xFFFFu) | (v.w << 16);
-    r.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
-    return r;
-}
-
-// Sum of the 32 activations of a chunk, from its 16 permuted pairs, in fp32
-// with a fixed order (pair 0 first).
-__device__ __forceinline__ float chunk_xsum(const h2 xp[16]) {
-    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc = __builtin_amdgcn_fdot2(xp[i], one, acc, false);
-    return acc;
-}
-
-// sum(code * x) over one chunk: codes and activations as 16 fp16 pairs in
-// matching order, exact products, fp32 accumulation starting from 0, pair 0
-// first.  Every kernel that needs this value calls this function (or
-// interleaves dequant_dword with the same sequence of dot steps).
-__device__ __forceinline__ float chunk_dot(const h2 codes[16], const h2 xp[16]) {
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc = __builtin_amdgcn_fdot2(codes[i], xp[i], acc, false);
-    return acc;
-}
-
-// One group-slice update of a lane's running row sum:
+// One group-slice update of a lane's running row sum (all in 2^-20 units):
 //   y += scale * sum(code*x) ; y += min * sum(x)
 // i.e. sum((code*scale + min) * x) over the slice, with each term once.
 __device__ __forceinline__ float group_update(float y, uint16_t s_bits, uint16_t m_bits, float dot, float xsum) {
