@@ -25,6 +25,13 @@ namespace q4 {
 // are requested before the activations are staged.
 // ---------------------------------------------------------------------------
 
+// Rank of workgroup b among the workgroups of its XCD, laid out XCD by XCD.
+__device__ __forceinline__ int xcd_block_order(int b, int grid) {
+    constexpr int kXcd = 8;
+    const int per = grid / kXcd, rem = grid % kXcd, x = b % kXcd;
+    return x * per + (x < rem ? x : rem) + b / kXcd;
+}
+
 template <int CPL>
 struct PassLoad {
     u4 q[CPL];
@@ -63,8 +70,10 @@ __device__ __forceinline__ void compute_pass(const PassLoad<CPL>& L, const h2 (&
     if (j == 0 && row < n) y[row] = yl;
 }
 
+constexpr int kGemvThreads = 512;  // 8 waves: two workgroups fill a CU at four waves per SIMD
+
 template <int LPR, int CPL>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kGemvThreads)
 gemv_reg_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
                 const uint16_t* __restrict__ mins, const uint16_t* __restrict__ x,
                 float* __restrict__ y, int n, int k) {
@@ -78,9 +87,12 @@ gemv_reg_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__
     const int rsub = lane / LPR;
     const long passes = ((long)n + RPW - 1) / RPW;
     const long W = (long)gridDim.x * (blockDim.x >> 6);
-    // Wave-major numbering: the passes of the last, partial round land on
-    // one wave of many different workgroups rather than on a few workgroups.
-    long p = (long)wave * gridDim.x + blockIdx.x;
+    // Workgroups are dealt to the 8 XCDs round-robin (block b on XCD b % 8).
+    // Renumber them so that consecutive numbers share an XCD: adjacent rows,
+    // whose scale/min bytes share cache lines, then meet in one L2.  Passes
+    // are numbered wave-major, so the last, partial round lands on one wave
+    // of many workgroups rather than on a few workgroups.
+    long p = (long)wave * gridDim.x + xcd_block_order(blockIdx.x, gridDim.x);
     auto row_of = [&](long pp) { return (int)(pp * RPW) + rsub; };
     auto clamp = [&](int r) { return r < n ? r : n - 1; };
 
@@ -229,7 +241,7 @@ int lanes_per_row(int k) {
 template <int LPR, int CPL>
 static hipError_t launch_reg(const GemvArgs& a, const DeviceInfo& dev, hipStream_t st) {
     constexpr int RPW = 64 / LPR;
-    constexpr int kThreads = 256;
+    constexpr int kThreads = kGemvThreads;
     const size_t lds = (size_t)a.k * 2;
     // Resident workgroups per CU for this instantiation (registers bound it;
     // the LDS footprint is at most 16 KB).  Queried once per process.

@@ -61,14 +61,24 @@ __device__ __forceinline__ void chunk_codes(const u4 q, h2 codes[16]) {
     }
 }
 
+// a.x * b.x + a.y * b.y + 0 in one instruction.  Equal to fdot2(a, b, 0.0f);
+// spelled out because the compiler otherwise zeroes a register and uses the
+// accumulating two-address form, one extra instruction per chain.
+__device__ __forceinline__ float dot2_first(h2 a, h2 b) {
+    float r;
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // sum(code * x) * 2^-20 over one chunk, from chunk_codes() and the 16
 // activation pairs in the same order.  Exact products; two fp32 chains
 // starting from 0 (pairs 0, 2, 4, ... and 1, 3, 5, ...), then
 // lo * 16 + hi in one fused multiply-add (the multiply is exact).  Every kernel that needs a chunk dot calls this.
 __device__ __forceinline__ float chunk_dot(const h2 codes[16], const h2 xp[16]) {
-    float lo = 0.0f, hi = 0.0f;
+    float lo = dot2_first(codes[0], xp[0]);
+    float hi = dot2_first(codes[1], xp[1]);
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
+    for (int i = 2; i < 16; i += 2) {
         lo = __builtin_amdgcn_fdot2(codes[i], xp[i], lo, false);
         hi = __builtin_amdgcn_fdot2(codes[i + 1], xp[i + 1], hi, false);
     }
