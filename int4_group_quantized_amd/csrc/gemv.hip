@@ -134,6 +134,147 @@ gemv_reg_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// Small-batch kernel with the batch-1 work mapping: the persistent pass walk
+// and two passes of weights in flight of gemv_reg_kernel, and BT activation
+// columns staged in LDS (permuted windows and per-chunk sums).  For every
+// column the per-lane arithmetic is compute_pass's, in the same order, and the
+// same butterfly finishes each row, so column b equals the batch-1 result for
+// X[b] bit for bit.  Columns b >= nb are zero and never stored.
+//
+// LDS layout, chunk c = j + t*LPR (lane j, slot t):
+//   windows  xq  [t][b][quad d][j]  (16 bytes each)
+//   sums     xsm [t][b][j]          (fp32)
+// so a lane's reads for slot t are one base address plus compile-time offsets
+// in (b, d), and the LPR lanes of a row read consecutive 16-byte words.
+// ---------------------------------------------------------------------------
+
+template <int LPR, int BT>
+__device__ __forceinline__ int cols_win_index(int c, int b, int d) {
+    return (((c / LPR) * BT + b) * 4 + d) * LPR + (c % LPR);
+}
+
+template <int LPR, int BT>
+__device__ __forceinline__ int cols_sum_index(int c, int b) {
+    return ((c / LPR) * BT + b) * LPR + (c % LPR);
+}
+
+template <int LPR, int CPL, int BT>
+__device__ __forceinline__ void compute_pass_cols(const PassLoad<CPL>& L, const u4* __restrict__ xq,
+                                                  const float* __restrict__ xsm, float* __restrict__ Y,
+                                                  int row, int n, int j, int nb) {
+    float y[BT];
+#pragma unroll
+    for (int b = 0; b < BT; ++b) y[b] = 0.0f;
+    // One column's windows and chunk sum are read from LDS one column ahead of
+    // their use; the scheduling barrier keeps the compiler from hoisting every
+    // column's reads, which would exhaust the registers.
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+        const u4* wt = xq + (size_t)t * BT * 4 * LPR + j;
+        const float* st = xsm + (size_t)t * BT * LPR + j;
+        h2 codes[16];
+        chunk_codes(L.q[t], codes);
+        u4 w[2][4];
+        float xs[2];
+        auto load_col = [&](int slot, int b) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) w[slot][d] = wt[(b * 4 + d) * LPR];
+            xs[slot] = st[b * LPR];
+        };
+        load_col(0, 0);
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+            if (b + 1 < BT) load_col((b + 1) & 1, b + 1);
+            h2 xp[16];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                xp[4 * d + 0] = as_h2(w[b & 1][d].x);
+                xp[4 * d + 1] = as_h2(w[b & 1][d].y);
+                xp[4 * d + 2] = as_h2(w[b & 1][d].z);
+                xp[4 * d + 3] = as_h2(w[b & 1][d].w);
+            }
+            y[b] = group_update(y[b], L.s[t], L.m[t], chunk_dot(codes, xp), xs[b & 1]);
+            // Pin the column's result here: without it the compiler sinks the
+            // dot chains below later columns and keeps every window live.
+            asm volatile("" : "+v"(y[b]));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < BT; ++b) {
+        const float v = reduce_lanes<LPR>(y[b]) * kInvUnit;
+        if (j == 0 && row < n && b < nb) Y[(size_t)b * (size_t)n + row] = v;
+    }
+}
+
+// Stage BT columns of X (zero past nb) in the layout above.
+template <int LPR, int BT>
+__device__ __forceinline__ void stage_columns(const uint16_t* __restrict__ X, u4* xq, float* xsm, int k, int nb) {
+    const int C = k >> 5;
+    const int wpc = k >> 3;  // windows per column
+    for (int w = threadIdx.x; w < BT * wpc; w += blockDim.x) {
+        const int b = w / wpc;
+        const int win = w - b * wpc;
+        u4 v = {0u, 0u, 0u, 0u};
+        if (b < nb) v = reinterpret_cast<const u4*>(X + (size_t)b * (size_t)k)[win];
+        xq[cols_win_index<LPR, BT>(win >> 2, b, win & 3)] = permute_window(v);
+    }
+    __syncthreads();
+    for (int w = threadIdx.x; w < BT * C; w += blockDim.x) {
+        const int b = w / C;
+        const int c = w - b * C;
+        h2 xp[16];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const u4 v = xq[cols_win_index<LPR, BT>(c, b, d)];
+            xp[4 * d + 0] = as_h2(v.x);
+            xp[4 * d + 1] = as_h2(v.y);
+            xp[4 * d + 2] = as_h2(v.z);
+            xp[4 * d + 3] = as_h2(v.w);
+        }
+        xsm[cols_sum_index<LPR, BT>(c, b)] = chunk_xsum(xp);
+    }
+    __syncthreads();
+}
+
+template <int LPR, int CPL, int BT>
+__global__ void __launch_bounds__(kGemvThreads)
+gemm_cols_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
+                 const uint16_t* __restrict__ mins, const uint16_t* __restrict__ X,
+                 float* __restrict__ Y, int n, int k, int nb) {
+    constexpr int RPW = 64 / LPR;
+    extern __shared__ u4 lds[];
+    const int C = k >> 5;
+    u4* xq = lds;                                                       // [CPL][BT][4][LPR]
+    float* xsm = reinterpret_cast<float*>(lds + (size_t)BT * 4 * C);   // [CPL][BT][LPR]
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int j = lane % LPR;
+    const int rsub = lane / LPR;
+    const long passes = ((long)n + RPW - 1) / RPW;
+    const long W = (long)gridDim.x * (blockDim.x >> 6);
+    long p = (long)wave * gridDim.x + xcd_block_order(blockIdx.x, gridDim.x);
+    auto row_of = [&](long pp) { return (int)(pp * RPW) + rsub; };
+    auto clamp = [&](int r) { return r < n ? r : n - 1; };
+
+    PassLoad<CPL> A, B;
+    if (p < passes) load_pass<LPR, CPL>(A, packed, scales, mins, clamp(row_of(p)), k, j);
+    if (p + W < passes) load_pass<LPR, CPL>(B, packed, scales, mins, clamp(row_of(p + W)), k, j);
+    stage_columns<LPR, BT>(X, xq, xsm, k, nb);
+
+    while (p < passes) {
+        compute_pass_cols<LPR, CPL, BT>(A, xq, xsm, Y, row_of(p), n, j, nb);
+        if (p + 2 * W < passes) load_pass<LPR, CPL>(A, packed, scales, mins, clamp(row_of(p + 2 * W)), k, j);
+        p += W;
+        if (p >= passes) break;
+        compute_pass_cols<LPR, CPL, BT>(B, xq, xsm, Y, row_of(p), n, j, nb);
+        if (p + 2 * W < passes) load_pass<LPR, CPL>(B, packed, scales, mins, clamp(row_of(p + 2 * W)), k, j);
+        p += W;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Batched kernel (also the batch-1 path when CPL > 4): BT activation columns
 // staged in LDS in permuted order with their per-chunk sums; the chunk loop
 // runs over t at run time.  Columns b >= nb are zero and never stored.
@@ -327,6 +468,51 @@ static hipError_t dispatch_batched(int lpr, int bt, const GemvArgs& a, const uin
     return hipErrorInvalidValue;
 }
 
+template <int LPR, int CPL, int BT>
+static hipError_t launch_cols(const GemvArgs& a, const uint16_t* X, float* Y, int nb, const DeviceInfo& dev,
+                              hipStream_t st) {
+    constexpr int RPW = 64 / LPR;
+    constexpr int kThreads = kGemvThreads;
+    const int C = a.k >> 5;
+    const size_t lds = (size_t)BT * 4 * C * 16 + (size_t)BT * C * 4;
+    // Per process: the LDS limit and the register footprint are the same on every gfx950 device.
+    static int per_cu = 0;
+    if (per_cu == 0) {
+        const void* fn = reinterpret_cast<const void*>(&gemm_cols_kernel<LPR, CPL, BT>);
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dev.max_lds);
+        if (e != hipSuccess) return e;
+        int nb_cu = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb_cu, fn, kThreads, lds);
+        if (e != hipSuccess) return e;
+        per_cu = nb_cu > 0 ? nb_cu : 1;
+    }
+    const long passes = ((long)a.n + RPW - 1) / RPW;
+    long grid = (long)dev.num_cu * per_cu;
+    const long need = (passes + (kThreads / 64) - 1) / (kThreads / 64);
+    if (grid > need) grid = need;
+    hipLaunchKernelGGL((gemm_cols_kernel<LPR, CPL, BT>), dim3((unsigned)grid), dim3(kThreads), lds, st,
+                       a.packed, a.scales, a.mins, X, Y, a.n, a.k, nb);
+    return hipGetLastError();
+}
+
+// Register-resident small-batch path for the (LPR, CPL) shapes that have one;
+// hipErrorNotSupported sends the caller to the generic batched kernel.
+static hipError_t dispatch_cols(int lpr, int cpl, int bt, const GemvArgs& a, const uint16_t* X, float* Y, int nb,
+                                const DeviceInfo& dev, hipStream_t st) {
+#define Q4_COLS(L, P)                                                          \
+    if (lpr == L && cpl == P) {                                                \
+        switch (bt) {                                                          \
+            case 2: return launch_cols<L, P, 2>(a, X, Y, nb, dev, st);         \
+            case 4: return launch_cols<L, P, 4>(a, X, Y, nb, dev, st);         \
+            case 8: return launch_cols<L, P, 8>(a, X, Y, nb, dev, st);         \
+            case 16: return launch_cols<L, P, 16>(a, X, Y, nb, dev, st);       \
+        }                                                                      \
+    }
+    Q4_COLS(32, 3) Q4_COLS(64, 4) Q4_COLS(16, 1) Q4_COLS(64, 1) Q4_COLS(64, 2)
+#undef Q4_COLS
+    return hipErrorNotSupported;
+}
+
 static int round_up_pow2_batch(int b) {
     int bt = 1;
     while (bt < b) bt <<= 1;
@@ -362,8 +548,10 @@ hipError_t launch_small_batch(const GemvArgs& a, const uint16_t* X, float* Y, in
     for (int b0 = 0; b0 < b; b0 += cap) {
         const int nb = (b - b0) < cap ? (b - b0) : cap;
         const int bt = round_up_pow2_batch(nb);
-        hipError_t e = dispatch_batched(lpr, bt, a, X + (size_t)b0 * (size_t)a.k,
-                                        Y + (size_t)b0 * (size_t)a.n, nb, dev, st);
+        const uint16_t* Xc = X + (size_t)b0 * (size_t)a.k;
+        float* Yc = Y + (size_t)b0 * (size_t)a.n;
+        hipError_t e = dispatch_cols(lpr, (a.k >> 5) / lpr, bt, a, Xc, Yc, nb, dev, st);
+        if (e == hipErrorNotSupported) e = dispatch_batched(lpr, bt, a, Xc, Yc, nb, dev, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
