@@ -237,8 +237,14 @@ __device__ __forceinline__ void stage_columns(const uint16_t* __restrict__ X, u4
     __syncthreads();
 }
 
+// 16 waves where the kernel fits in 128 registers (LPR <= 32, CPL <= 3): one
+// workgroup holds the columns in LDS and four waves per SIMD hide the LDS
+// latency of the column loop; 8 waves otherwise.
+template <int LPR, int CPL>
+constexpr int cols_threads() { return (LPR <= 32 && CPL <= 3) ? 1024 : 512; }
+
 template <int LPR, int CPL, int BT>
-__global__ void __launch_bounds__(kGemvThreads)
+__global__ void __launch_bounds__((cols_threads<LPR, CPL>()))
 gemm_cols_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
                  const uint16_t* __restrict__ mins, const uint16_t* __restrict__ X,
                  float* __restrict__ Y, int n, int k, int nb) {
@@ -472,7 +478,7 @@ template <int LPR, int CPL, int BT>
 static hipError_t launch_cols(const GemvArgs& a, const uint16_t* X, float* Y, int nb, const DeviceInfo& dev,
                               hipStream_t st) {
     constexpr int RPW = 64 / LPR;
-    constexpr int kThreads = kGemvThreads;
+    constexpr int kThreads = cols_threads<LPR, CPL>();
     const int C = a.k >> 5;
     const size_t lds = (size_t)BT * 4 * C * 16 + (size_t)BT * C * 4;
     // Per process: the LDS limit and the register footprint are the same on every gfx950 device.
