@@ -84,6 +84,10 @@ def test_dyadic_bit_exact(dev, n, k):
         assert np.array_equal(Yb, np.tile(ref, (5, 1)))
         Yp = cpu(q4.q4g128_gemm_prefill(packed, s, m, X)).astype(np.float64)
         assert np.array_equal(Yp, np.tile(ref, (5, 1)))
+        for mtok in (70, 200):  # the wide prompt-processing kernel
+            Xw = xd.reshape(1, -1).repeat(mtok, 1).contiguous()
+            Yw = cpu(q4.q4g128_gemm_prefill(packed, s, m, Xw)).astype(np.float64)
+            assert np.array_equal(Yw, np.tile(ref, (mtok, 1)))
 
 
 # --------------------------------------------------------------------------
@@ -187,7 +191,8 @@ def test_non_default_stream(dev):
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("mtok,n,k", [(1, 64, 128), (2, 70, 384), (15, 100, 512), (16, 128, 3072), (17, 65, 3072),
-                                      (34, 200, 3072), (100, 33, 8192), (112, 128, 1024), (300, 64, 2048),
+                                      (34, 200, 3072), (64, 129, 256), (65, 130, 640), (100, 33, 8192),
+                                      (112, 128, 1024), (129, 300, 1536), (193, 45, 384), (300, 64, 2048),
                                       (5, 40, 32768)])
 def test_prefill_parity_shapes(dev, mtok, n, k):
     w = synth.weights(n, k, seed=mtok * 1000 + n)
