@@ -121,6 +121,12 @@ def time_eager(torch, stream, launch, steps, warmup):
     return start.elapsed_time(stop) / steps
 
 
+def time_checked(torch, stream, launch, out, steps, warmup, n_graph):
+    """Eager ms per call, after checking that a HIP graph of the same launches rewrites `out` identically."""
+    time_graph(torch, stream, launch, n_graph, n_graph, warmup, out=out)
+    return time_eager(torch, stream, launch, steps, warmup)
+
+
 def gemv_launcher(q4, rot, x, y):
     lib = q4.library()
     ptrs = [(p.data_ptr(), s.data_ptr(), m.data_ptr()) for p, s, m in rot.sets]
@@ -263,20 +269,23 @@ def main():
     launch = gemv_launcher(q4, rot, xd, y)
     nbytes = algorithmic_bytes(n, k, 1)
 
-    ms_graph, launches, _g = time_graph(torch, stream, launch, GRAPH_LAUNCHES, args.steps, args.warmup, out=y)
-    ms_eager = time_eager(torch, stream, launch, min(args.steps, 1000), args.warmup)
+    # Primary: back-to-back launches on one stream (how a caller drives the
+    # library).  Cross-check: the same launches replayed from a HIP graph,
+    # which must rewrite the output with the eager result.
+    ms_eager = time_eager(torch, stream, launch, args.steps, args.warmup)
+    ms_graph, _launches, _g = time_graph(torch, stream, launch, GRAPH_LAUNCHES, args.steps, args.warmup, out=y)
     graph_matches_eager = True  # checked inside time_graph
 
-    gbs = nbytes / (ms_graph * 1e-3) / 1e9
+    gbs = nbytes / (ms_eager * 1e-3) / 1e9
     traffic, traffic_note = read_traffic(nbytes)
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": launches,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_graph, 6),
+        "ms_per_step": round(ms_eager, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -287,11 +296,11 @@ def main():
             "n": n, "k": k, "batch": 1,
             "bytes_per_call": nbytes,
             "weight_copies_rotated": rot.copies,
-            "timing": f"HIP graph of {GRAPH_LAUNCHES} launches, HIP events on the launch stream",
+            "timing": "back-to-back launches on one stream, HIP events on the launch stream",
         },
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "us_per_call": round(ms_graph * 1e3, 3),
-        "us_per_call_eager": round(ms_eager * 1e3, 3),
+        "us_per_call": round(ms_eager * 1e3, 3),
+        "us_per_call_graph": round(ms_graph * 1e3, 3),
         "graph_matches_eager": graph_matches_eager,
         "roofline": {
             "bound": "hbm",
@@ -311,8 +320,7 @@ def main():
             ww, xx = synth.gemv_case(nn, kk, sd)
             r = Rotation(torch, q4, ww, dev)
             yy = torch.empty(nn, dtype=torch.float32, device=dev)
-            ms, _, _ = time_graph(torch, stream, gemv_launcher(q4, r, f16(xx[0]), yy), GRAPH_LAUNCHES,
-                                  1000, 20, out=yy)
+            ms = time_checked(torch, stream, gemv_launcher(q4, r, f16(xx[0]), yy), yy, 1000, 20, GRAPH_LAUNCHES)
             b = algorithmic_bytes(nn, kk, 1)
             del r
             return {"us_per_call": round(ms * 1e3, 3), "GB_per_s": round(b / (ms * 1e-3) / 1e9, 1),
@@ -323,17 +331,16 @@ def main():
         for b in (2, 4, 8, 16):
             X = f16(synth.batch_activations(b))
             Y = torch.empty((b, n), dtype=torch.float32, device=dev)
-            ms, _, _ = time_graph(torch, stream, batch_launcher(q4, rot, X, Y, b), GRAPH_LAUNCHES, 1000, 20,
-                                  out=Y)
+            ms = time_checked(torch, stream, batch_launcher(q4, rot, X, Y, b), Y, 1000, 20, GRAPH_LAUNCHES)
             bb = algorithmic_bytes(n, k, b)
             forms[f"fused_25088x3072_small_batch_b{b}"] = {
                 "us_per_call": round(ms * 1e3, 3), "GB_per_s": round(bb / (ms * 1e-3) / 1e9, 1),
                 "frac_hbm": round(bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "speedup_vs_b_calls": round(b * ms_graph / ms, 3)}
+                "speedup_vs_b_calls": round(b * ms_eager / ms, 3)}
         for mtok in (34, 256):
             X = f16(synth.prefill_activations(mtok))
             Y = torch.empty((mtok, n), dtype=torch.float32, device=dev)
-            ms, _, _ = time_graph(torch, stream, prefill_launcher(q4, rot, X, Y, mtok), 20, 200, 5, out=Y)
+            ms = time_checked(torch, stream, prefill_launcher(q4, rot, X, Y, mtok), Y, 200, 5, 20)
             bb = algorithmic_bytes(n, k, mtok)
             flops = 2.0 * mtok * n * k
             forms[f"fused_25088x3072_prefill_m{mtok}"] = {
