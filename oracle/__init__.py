@@ -1,4 +1,4 @@
-"""CPU oracle (fp64, NumPy) for the int4 group-128 GEMV family.
+"""CPU oracle (NumPy) for the int4 group-128 GEMV family and its export step.
 
 TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
 benchmark's CPU-baseline leg, never by the GPU library or its binding.
@@ -14,3 +14,4 @@ from .q4g128 import (  # noqa: F401
     term_magnitude,
     unpack,
 )
+from .quantize import quantize  # noqa: F401,E402

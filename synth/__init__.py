@@ -61,6 +61,21 @@ def draw_weights(rng: np.random.Generator, n: int, k: int) -> Weights:
     return Weights(codes, scales, mins)
 
 
+def draw_float_weights(rng: np.random.Generator, n: int, k: int) -> np.ndarray:
+    """float32 [N][K] stand-in for trained projection weights (input of the export step).
+
+    Normal values with a per-row spread drawn uniformly on [0.005, 0.05]; the
+    pages print no weights, so only the shape of the distribution matters.
+    """
+    spread = rng.uniform(0.005, 0.05, (n, 1))
+    return (rng.standard_normal((n, k)) * spread).astype(np.float32)
+
+
+def float_weights(n: int, k: int, seed: int) -> np.ndarray:
+    """float32 weights of one matrix drawn from their own generator."""
+    return draw_float_weights(_rng(seed), n, k)
+
+
 def draw_activations(rng: np.random.Generator, b: int, k: int) -> np.ndarray:
     return rng.standard_normal((b, k)).astype(np.float16)
 
@@ -98,6 +113,7 @@ SEEDS = {
     "batch_x": 4,
     "prefill_x34": 5,
     "prefill_x256": 6,
+    "float_weights": 21,
 }
 
 
