@@ -4,12 +4,14 @@
 One step = one q4g128_gemv call on the fused 25,088 x 3,072 projection at
 batch 1 (packed weights + fp16 scales + fp16 mins + fp16 activations in,
 fp32 out).  Weight copies totalling >= 512 MB are rotated so that the 256 MB
-Infinity Cache cannot serve repeated calls; the timed launches are replayed
-from one HIP graph captured on the benchmark's stream, bracketed by HIP
-events on that stream.
+Infinity Cache cannot serve repeated calls.  The timed launches go back to
+back on the benchmark's stream, bracketed by HIP events on that stream; the
+same launches replayed from a HIP graph are timed as a cross-check that must
+reproduce the eager output.
 
 Prints ONE JSON line.  Extra forms (other shapes, small batch, prompt
-processing, the 36-layer stack) are reported under "forms".
+processing, the export quantiser, the 36-layer stack) are reported under
+"forms".
 """
 from __future__ import annotations
 
@@ -166,6 +168,24 @@ def prefill_launcher(q4, rot, X, Y, mtok):
         rc = lib.q4g128_gemm_prefill(p, s, m, xp, yp, n, k, mtok, st)
         if rc != 0:
             raise RuntimeError(f"q4g128_gemm_prefill failed: {q4.q4g128_status_string(rc)}")
+    return launch
+
+
+def quantize_bytes(n: int, k: int) -> int:
+    """float32 weights read + packed codes, fp16 scales and fp16 mins written."""
+    return n * k * 4 + n * k // 2 + 2 * n * (k // 128) * 2
+
+
+def quantize_launcher(q4, Ws, packed, scales, mins, n, k):
+    lib = q4.library()
+    ptrs = [W.data_ptr() for W in Ws]
+    pp, sp, mp = packed.data_ptr(), scales.data_ptr(), mins.data_ptr()
+    R = len(ptrs)
+
+    def launch(i, st):
+        rc = lib.q4g128_quantize(ptrs[i % R], pp, sp, mp, n, k, st)
+        if rc != 0:
+            raise RuntimeError(q4.q4g128_status_string(rc))
     return launch
 
 
@@ -349,6 +369,20 @@ def main():
                 "TFLOP_per_s": round(flops / (ms * 1e-3) / 1e12, 1),
                 "frac_mfma_f16": round(flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
         del rot
+        torch.cuda.empty_cache()
+        # export quantiser on the fused projection's float32 weights
+        Wf = torch.from_numpy(synth.float_weights(n, k, synth.SEEDS["float_weights"])).to(dev)
+        Ws = [Wf] + [Wf.clone() for _ in range(max(0, -(-MALL_DEFEAT_BYTES // (n * k * 4)) - 1))]
+        Pq = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+        Sq = torch.empty((n, k // 128), dtype=torch.float16, device=dev)
+        Mq = torch.empty((n, k // 128), dtype=torch.float16, device=dev)
+        ms = time_checked(torch, stream, quantize_launcher(q4, Ws, Pq, Sq, Mq, n, k), Pq, 200, 5, 10)
+        qb = quantize_bytes(n, k)
+        forms["fused_25088x3072_quantize"] = {
+            "us_per_call": round(ms * 1e3, 3), "GB_per_s": round(qb / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(qb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "copies_rotated": len(Ws),
+            "bytes_per_call": qb}
+        del Ws, Wf, Pq, Sq, Mq
         torch.cuda.empty_cache()
     if args.stack:
         forms["stack_36x3_gemv_b1"] = time_stack(torch, q4, dev, stream, f16)

@@ -57,7 +57,7 @@ typedef int32_t q4_status;
 /* K not a positive multiple of 128, K above 32768, or N / M above
    Q4G128_MAX_N. */
 #define Q4_ESHAPE (-2)
-/* codes / packed / x / X not 16-byte aligned; scales / mins not 2-byte
+/* codes / packed / x / X / W not 16-byte aligned; scales / mins not 2-byte
    aligned; y / Y not 4-byte aligned. */
 #define Q4_EALIGN (-3)
 /* The HIP runtime reported an error while querying the device or launching;
@@ -78,6 +78,29 @@ typedef int32_t q4_status;
  */
 Q4_API q4_status q4g128_pack(const uint8_t* codes, uint8_t* packed,
                       int64_t n, int64_t k, void* stream);
+
+/*
+ * q4g128_quantize -- export float32 weights to the format above.
+ * The rumik write-up ("Step 3") exports every projection with a short CPU
+ * job: groups of 128 columns, one fp16 scale and one fp16 minimum per group.
+ * The pages give no formula; the reading implemented is the min/max affine
+ * quantiser that the dequantisation w = code*scale + min implies.  For each
+ * group, with every step one IEEE fp32 operation rounded to nearest even:
+ *     lo = min, hi = max of the group's 128 values
+ *     min   = fp16(lo + 0)            (a zero minimum is stored as +0)
+ *     scale = fp16((hi - lo) / 15)
+ *     code  = clamp(round_half_even((w - min) / scale), 0, 15) against the
+ *             stored fp16 min and scale; code 0 everywhere if scale == 0.
+ *   W      [N][K] float32, row-major, finite with |w| <= 65504 (other values
+ *          give unspecified codes, never a fault).
+ *   packed [N][K/2], scales [N][K/128], mins [N][K/128]: written in full.
+ * Errors: Q4_EINVAL for a NULL pointer, N <= 0 or outputs that overlap W or
+ * each other; Q4_ESHAPE for K outside the limits or more than 2^36 groups;
+ * Q4_EALIGN unless W and packed are 16-byte and scales / mins 2-byte
+ * aligned.  Untimed set-up work, not part of the decode step.
+ */
+Q4_API q4_status q4g128_quantize(const float* W, uint8_t* packed, uint16_t* scales,
+                          uint16_t* mins, int64_t n, int64_t k, void* stream);
 
 /*
  * q4g128_gemv -- y[n] = sum_k w[n][k] * x[k]   (batch-1 decode product).

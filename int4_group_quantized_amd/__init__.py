@@ -32,6 +32,7 @@ MAX_BATCH = 16
 
 EXPORTED = (
     "q4g128_pack",
+    "q4g128_quantize",
     "q4g128_gemv",
     "q4g128_gemm_small_batch",
     "q4g128_gemm_prefill",
@@ -52,16 +53,17 @@ class Q4Error(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m int4_group_quantized_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python int4_group_quantized_amd/build.py` "
             "(or __graft_entry__.build()); there is no fallback implementation"
         )
     lib = ctypes.CDLL(LIB_PATH)
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.q4g128_pack.argtypes = [vp, vp, i64, i64, vp]
+    lib.q4g128_quantize.argtypes = [vp, vp, vp, vp, i64, i64, vp]
     lib.q4g128_gemv.argtypes = [vp, vp, vp, vp, vp, i64, i64, vp]
     lib.q4g128_gemm_small_batch.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.q4g128_gemm_prefill.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
-    for name in ("q4g128_pack", "q4g128_gemv", "q4g128_gemm_small_batch", "q4g128_gemm_prefill"):
+    for name in ("q4g128_pack", "q4g128_quantize", "q4g128_gemv", "q4g128_gemm_small_batch", "q4g128_gemm_prefill"):
         getattr(lib, name).restype = ctypes.c_int32
     lib.q4g128_status_string.argtypes = [ctypes.c_int32]
     lib.q4g128_status_string.restype = ctypes.c_char_p
@@ -133,6 +135,29 @@ def q4g128_pack(codes: torch.Tensor, packed: torch.Tensor = None, stream=None) -
     with torch.cuda.device(dev):
         _check(_lib.q4g128_pack(codes.data_ptr(), packed.data_ptr(), n, k, _stream(dev, stream)), "q4g128_pack")
     return packed
+
+
+def q4g128_quantize(W: torch.Tensor, packed=None, scales=None, mins=None, stream=None):
+    """float32 W [N][K] -> (packed uint8 [N][K/2], scales fp16 [N][K/128], mins fp16 [N][K/128])."""
+    if W.dim() != 2:
+        raise ValueError("W must be [N][K]")
+    n, k = W.shape
+    _dev_tensor(W, "W", torch.float32, (n, k))
+    g = k // GROUP
+    if packed is None:
+        packed = torch.empty((n, k // 2), dtype=torch.uint8, device=W.device)
+    if scales is None:
+        scales = torch.empty((n, g), dtype=torch.float16, device=W.device)
+    if mins is None:
+        mins = torch.empty((n, g), dtype=torch.float16, device=W.device)
+    _dev_tensor(packed, "packed", torch.uint8, (n, k // 2))
+    _dev_tensor(scales, "scales", torch.float16, (n, g))
+    _dev_tensor(mins, "mins", torch.float16, (n, g))
+    dev = _same_device(W, packed, scales, mins)
+    with torch.cuda.device(dev):
+        _check(_lib.q4g128_quantize(W.data_ptr(), packed.data_ptr(), scales.data_ptr(), mins.data_ptr(), n, k,
+                                    _stream(dev, stream)), "q4g128_quantize")
+    return packed, scales, mins
 
 
 def q4g128_gemv(packed, scales, mins, x, y=None, stream=None) -> torch.Tensor:

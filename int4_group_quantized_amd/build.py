@@ -1,6 +1,8 @@
 """Build libq4g128.so (the C-ABI library) in-tree with hipcc for gfx950.
 
-Usage:  python -m int4_group_quantized_amd.build   (or call build_library()).
+Usage:  python int4_group_quantized_amd/build.py   (or call build_library()).
+Run it as a script, not as a module of the package: importing the package
+loads the library that this script replaces.
 The shared object is written next to this file so that it travels with the
 source tree; intermediate objects go to _build/ (not committed).
 """
@@ -20,7 +22,7 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libq4g128.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["api.cpp", "gemv.hip", "prefill.hip", "pack.hip"]
+SOURCES = ["api.cpp", "gemv.hip", "prefill.hip", "pack.hip", "quantize.hip"]
 ARCH = "gfx950"
 
 

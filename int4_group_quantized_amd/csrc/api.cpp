@@ -109,6 +109,23 @@ q4_status q4g128_pack(const uint8_t* codes, uint8_t* packed, int64_t n, int64_t 
     return e == hipSuccess ? Q4_OK : device_error(e);
 }
 
+q4_status q4g128_quantize(const float* W, uint8_t* packed, uint16_t* scales, uint16_t* mins, int64_t n,
+                          int64_t k, void* stream) {
+    if (!W || !packed || !scales || !mins) return Q4_EINVAL;
+    q4_status s = check_nk(n, k);
+    if (s != Q4_OK) return s;
+    const size_t groups = (size_t)n * (size_t)(k / Q4G128_GROUP);
+    if (groups > (size_t)q4::kQuantizeMaxGroups) return Q4_ESHAPE;
+    if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(mins, 2)) return Q4_EALIGN;
+    const size_t wbytes = (size_t)n * (size_t)k * 4, pbytes = (size_t)n * (size_t)k / 2, gbytes = groups * 2;
+    if (overlaps(packed, pbytes, W, wbytes) || overlaps(scales, gbytes, W, wbytes) ||
+        overlaps(mins, gbytes, W, wbytes) || overlaps(packed, pbytes, scales, gbytes) ||
+        overlaps(packed, pbytes, mins, gbytes) || overlaps(scales, gbytes, mins, gbytes))
+        return Q4_EINVAL;
+    hipError_t e = q4::launch_quantize(W, packed, scales, mins, n, k, (hipStream_t)stream);
+    return e == hipSuccess ? Q4_OK : device_error(e);
+}
+
 q4_status q4g128_gemv(const uint8_t* packed, const uint16_t* scales, const uint16_t* mins,
                       const uint16_t* x, float* y, int64_t n, int64_t k, void* stream) {
     q4_status s = check_product(packed, scales, mins, x, y, n, k, 1);
@@ -154,7 +171,7 @@ const char* q4g128_status_string(q4_status status) {
         case Q4_OK: return "Q4_OK: success";
         case Q4_EINVAL: return "Q4_EINVAL: null pointer, non-positive size, batch outside 1..16 or overlapping output";
         case Q4_ESHAPE: return "Q4_ESHAPE: K must be a multiple of 128 in [128, 32768]; sizes must fit the kernels' index range";
-        case Q4_EALIGN: return "Q4_EALIGN: packed/codes/activations need 16-byte, scales/mins 2-byte, outputs 4-byte alignment";
+        case Q4_EALIGN: return "Q4_EALIGN: packed/codes/activations/float weights need 16-byte, scales/mins 2-byte, outputs 4-byte alignment";
         case Q4_EDEVICE: return "Q4_EDEVICE: the HIP runtime reported an error (see q4g128_last_hip_error)";
     }
     return "unknown q4g128 status";

@@ -28,6 +28,9 @@ struct GemvArgs {
 int lanes_per_row(int k);
 
 hipError_t launch_pack(const uint8_t* codes, uint8_t* packed, int64_t n, int64_t k, hipStream_t st);
+hipError_t launch_quantize(const float* W, uint8_t* packed, uint16_t* scales, uint16_t* mins, int64_t n,
+                           int64_t k, hipStream_t st);
+constexpr long kQuantizeMaxGroups = 0x7FFFFFFFL * 32L;  // grid limit of the export kernel
 hipError_t launch_gemv(const GemvArgs& a, const DeviceInfo& dev, hipStream_t st);
 hipError_t launch_small_batch(const GemvArgs& a, const uint16_t* X, float* Y, int b,
                               const DeviceInfo& dev, hipStream_t st);

@@ -14,6 +14,7 @@ w = code * scale + min:
 
   1. per group, lo = min and hi = max of its 128 values;
   2. min   = fp16(lo), scale = fp16(fl32(hi - lo) / 15)   (15 = top code);
+     a zero minimum is stored as +0 (lo + 0 in fp32 turns -0 into +0);
   3. code  = clamp(round_half_even((w - min) / scale), 0, 15), computed
      against the STORED fp16 min and scale, so that the code is the nearest
      one under the dequantisation that will actually be applied;
@@ -58,7 +59,7 @@ def quantize(W: np.ndarray):
     span = hi - lo                                         # fp32, rounded once
     scale32 = span / np.float32(TOP_CODE)                  # fp32, rounded once
     scales = scale32.astype(np.float16)                    # step 2: round to nearest even
-    mins = lo.astype(np.float16)
+    mins = (lo + np.float32(0)).astype(np.float16)         # -0 -> +0, then nearest even
 
     s = scales.astype(np.float32)[:, :, None]              # the stored values, exactly
     m = mins.astype(np.float32)[:, :, None]

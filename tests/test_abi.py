@@ -65,12 +65,18 @@ def pack(c=X, p=P, n=64, k=256):
     return q4.library().q4g128_pack(c, p, n, k, None)
 
 
+def quantize(w=X, p=P, s=S, m=M, n=64, k=256):
+    return q4.library().q4g128_quantize(w, p, s, m, n, k, None)
+
+
 @pytest.mark.parametrize("call", [
     lambda: gemv(p=None), lambda: gemv(s=None), lambda: gemv(m=None), lambda: gemv(x=None),
     lambda: gemv(y=None), lambda: gemv(n=0), lambda: gemv(n=-5),
     lambda: batch(0), lambda: batch(17), lambda: batch(-1), lambda: batch(4, x=None),
     lambda: prefill(0), lambda: prefill(-3), lambda: prefill(34, y=None),
     lambda: pack(c=None), lambda: pack(p=None), lambda: pack(n=0),
+    lambda: quantize(w=None), lambda: quantize(p=None), lambda: quantize(s=None), lambda: quantize(m=None),
+    lambda: quantize(n=0), lambda: quantize(n=-2),
 ])
 def test_einval(call):
     assert call() == EINVAL
@@ -83,11 +89,29 @@ def test_eshape_k(k):
     assert batch(3, k=k) == expect
     assert prefill(5, k=k) == expect
     assert pack(k=k) == expect
+    assert quantize(k=k) == expect
 
 
 def test_eshape_sizes():
     assert gemv(n=1 << 31) == ESHAPE
     assert prefill(1 << 31) == ESHAPE
+    assert quantize(n=1 << 31) == ESHAPE
+    # more groups than the export kernel's grid covers: N * K/128 > 2^36
+    assert quantize(n=(1 << 31) - 256, k=32768) == ESHAPE
+
+
+@pytest.mark.parametrize("which", ["w", "p", "s", "m"])
+def test_quantize_ealign(which):
+    bad = {"w": X + 4, "p": P + 8, "s": S + 1, "m": M + 1}[which]
+    assert quantize(**{which: bad}) == EALIGN
+    assert quantize(s=S + 2, m=M + 2, n=0) == EINVAL  # 2-byte scales / mins pass alignment
+
+
+def test_quantize_overlaps_rejected():
+    assert quantize(p=X + 64) == EINVAL   # packed inside W
+    assert quantize(s=X + 128) == EINVAL  # scales inside W
+    assert quantize(m=P + 32) == EINVAL   # mins inside packed
+    assert quantize(m=S + 64) == EINVAL   # mins inside scales
 
 
 @pytest.mark.parametrize("which", ["p", "x", "s", "m", "y"])
