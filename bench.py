@@ -348,6 +348,8 @@ def main():
 
         forms["oproj_3072x3072_gemv_b1"] = gemv_form("oproj_3072x3072")
         forms["down_3072x8192_gemv_b1"] = gemv_form("down_3072x8192")
+        for name in ("pages_fused_25088x2048", "pages_oproj_2048x2048", "pages_down_2048x11008"):
+            forms[name + "_gemv_b1"] = gemv_form(name)
         for b in (2, 4, 8, 16):
             X = f16(synth.batch_activations(b))
             Y = torch.empty((b, n), dtype=torch.float32, device=dev)
@@ -383,6 +385,9 @@ def main():
             "frac_hbm": round(qb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "copies_rotated": len(Ws),
             "bytes_per_call": qb}
         del Ws, Wf, Pq, Sq, Mq
+        torch.cuda.empty_cache()
+    if not args.no_forms:
+        forms["pages_stack_36x3_hidden2048_gemv_b1"] = time_pages_stack(torch, q4, dev, stream, f16)
         torch.cuda.empty_cache()
     if args.stack:
         forms["stack_36x3_gemv_b1"] = time_stack(torch, q4, dev, stream, f16)
@@ -426,6 +431,46 @@ def time_stack(torch, q4, dev, stream, f16):
     return {"us_per_step": round(ms * 1e3, 2), "launches": len(calls), "bytes": total,
             "GB_per_s": round(total / (ms * 1e-3) / 1e9, 1),
             "frac_hbm": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def time_pages_stack(torch, q4, dev, stream, f16):
+    """The pages' decode step shape: 36 layers x (fused 25,088x2,048,
+    o_proj 2,048x2,048, down 2,048x11,008) GEMVs in one graph of 108 launches.
+
+    One seeded weight set per shape is drawn on the host; every layer gets its
+    own device copy of it (distinct memory, 1.4 GB in total, so the 256 MB
+    Infinity Cache cannot serve one layer's weights to the next).
+    """
+    names = ["pages_fused_25088x2048", "pages_oproj_2048x2048", "pages_down_2048x11008"]
+    lib = q4.library()
+    base = []
+    for name in names:
+        ww, xx = synth.workload(name)
+        codes = torch.from_numpy(ww.codes).to(dev)
+        base.append((q4.q4g128_pack(codes), f16(ww.scales), f16(ww.mins), f16(xx[0]), ww.n, ww.k))
+        del codes
+    keep, calls, total = [], [], 0
+    for _layer in range(synth.STACK_LAYERS):
+        for packed, s, m, xx, nn, kk in base:
+            p2, s2, m2 = packed.clone(), s.clone(), m.clone()
+            yy = torch.empty(nn, dtype=torch.float32, device=dev)
+            keep.append((p2, s2, m2, yy))
+            calls.append((p2.data_ptr(), s2.data_ptr(), m2.data_ptr(), xx.data_ptr(), yy.data_ptr(), nn, kk))
+            total += algorithmic_bytes(nn, kk, 1)
+    torch.cuda.synchronize()
+
+    def launch_all(_i, st):
+        for c in calls:
+            rc = lib.q4g128_gemv(*c, st)
+            if rc != 0:
+                raise RuntimeError(q4.q4g128_status_string(rc))
+    ms, _reps, _ = time_graph(torch, stream, launch_all, 1, 20, 2)
+    out = {"us_per_step": round(ms * 1e3, 2), "launches": len(calls), "bytes": total,
+           "GB_per_s": round(total / (ms * 1e-3) / 1e9, 1),
+           "frac_hbm": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "weights": "one seeded set per shape, a device copy per layer"}
+    del keep
+    return out
 
 
 if __name__ == "__main__":

@@ -3,8 +3,15 @@
 // Work mapping (depends on K only, never on the batch size, so that every
 // batched output column repeats the batch-1 arithmetic bit for bit):
 //   C   = K / 32 chunks per row (a chunk = 16 packed bytes = 32 codes);
-//   LPR = lanes per row, the largest of 64, 32, 16, 8, 4 dividing C;
-//   CPL = C / LPR chunks per lane; lane j of a row owns chunks j + t*LPR.
+//   LPR = lanes per row: the largest of 64, 32, 16 dividing C; otherwise 64
+//         if C > 64 ("ragged": the last chunk column of a row is partial),
+//         else the largest of 8, 4 dividing C;
+//   CPL = ceil(C / LPR) chunks per lane; lane j of a row owns chunks
+//         j + t*LPR that are below C.  A ragged lane's missing chunk is
+//         either skipped or fed zero activations, which leaves its sum
+//         unchanged bit for bit (fma(s, +0, y) and fma(m, +0, y) return y
+//         for any y other than -0, and a lane sum starting at +0 never
+//         becomes -0), so every kernel computes the same bits.
 // A wave therefore covers RPW = 64 / LPR rows per "pass"; one load
 // instruction of a wave reads RPW contiguous segments of LPR * 16 bytes.
 // Per lane and chunk: codes as exact fp16 denormals (chunk_codes), exact
@@ -39,18 +46,34 @@ struct PassLoad {
     uint16_t m[CPL];
 };
 
-template <int LPR, int CPL>
+// Chunks past C (ragged rows only) load the row's last chunk instead: every
+// load stays in range, and the chunk's activations are zero.
+template <int LPR, int CPL, bool RAGGED = false>
 __device__ __forceinline__ void load_pass(PassLoad<CPL>& L, const uint8_t* __restrict__ packed,
                                           const uint16_t* __restrict__ scales,
                                           const uint16_t* __restrict__ mins, int rowc, int k, int j) {
     const int G = k >> 7;
-    const u4* rp = reinterpret_cast<const u4*>(packed + (size_t)rowc * (size_t)(k >> 1)) + j;
-    const size_t g0 = (size_t)rowc * (size_t)G + (size_t)(j >> 2);
+    if constexpr (!RAGGED) {
+        const u4* rp = reinterpret_cast<const u4*>(packed + (size_t)rowc * (size_t)(k >> 1)) + j;
+        const size_t g0 = (size_t)rowc * (size_t)G + (size_t)(j >> 2);
 #pragma unroll
-    for (int t = 0; t < CPL; ++t) {
-        L.q[t] = __builtin_nontemporal_load(rp + t * LPR);
-        L.s[t] = scales[g0 + t * (LPR / 4)];
-        L.m[t] = mins[g0 + t * (LPR / 4)];
+        for (int t = 0; t < CPL; ++t) {
+            L.q[t] = __builtin_nontemporal_load(rp + t * LPR);
+            L.s[t] = scales[g0 + t * (LPR / 4)];
+            L.m[t] = mins[g0 + t * (LPR / 4)];
+        }
+    } else {
+        const int C = k >> 5;
+        const u4* rp = reinterpret_cast<const u4*>(packed + (size_t)rowc * (size_t)(k >> 1));
+        const uint16_t* sp = scales + (size_t)rowc * (size_t)G;
+        const uint16_t* mp = mins + (size_t)rowc * (size_t)G;
+#pragma unroll
+        for (int t = 0; t < CPL; ++t) {
+            const int c = j + t * LPR < C ? j + t * LPR : C - 1;
+            L.q[t] = __builtin_nontemporal_load(rp + c);
+            L.s[t] = sp[c >> 2];
+            L.m[t] = mp[c >> 2];
+        }
     }
 }
 
@@ -72,7 +95,7 @@ __device__ __forceinline__ void compute_pass(const PassLoad<CPL>& L, const h2 (&
 
 constexpr int kGemvThreads = 512;  // 8 waves: two workgroups fill a CU at four waves per SIMD
 
-template <int LPR, int CPL>
+template <int LPR, int CPL, bool RAGGED>
 __global__ void __launch_bounds__(kGemvThreads)
 gemv_reg_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
                 const uint16_t* __restrict__ mins, const uint16_t* __restrict__ x,
@@ -97,8 +120,8 @@ gemv_reg_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__
     auto clamp = [&](int r) { return r < n ? r : n - 1; };
 
     PassLoad<CPL> A, B;
-    if (p < passes) load_pass<LPR, CPL>(A, packed, scales, mins, clamp(row_of(p)), k, j);
-    if (p + W < passes) load_pass<LPR, CPL>(B, packed, scales, mins, clamp(row_of(p + W)), k, j);
+    if (p < passes) load_pass<LPR, CPL, RAGGED>(A, packed, scales, mins, clamp(row_of(p)), k, j);
+    if (p + W < passes) load_pass<LPR, CPL, RAGGED>(B, packed, scales, mins, clamp(row_of(p + W)), k, j);
 
     // Stage x: window w (8 halves) = quad (w & 3) of chunk (w >> 2).
     const u4* xv = reinterpret_cast<const u4*>(x);
@@ -111,9 +134,15 @@ gemv_reg_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__
 #pragma unroll
     for (int t = 0; t < CPL; ++t) {
         const int c = j + t * LPR;
+        const bool valid = !RAGGED || c < C;
+        const uint32_t keep = valid ? 0xFFFFFFFFu : 0u;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            const u4 v = x_lds[d * C + c];
+            u4 v = x_lds[d * C + (valid ? c : C - 1)];
+            v.x &= keep;
+            v.y &= keep;
+            v.z &= keep;
+            v.w &= keep;
             xp[t][4 * d + 0] = as_h2(v.x);
             xp[t][4 * d + 1] = as_h2(v.y);
             xp[t][4 * d + 2] = as_h2(v.z);
@@ -124,11 +153,13 @@ gemv_reg_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__
 
     while (p < passes) {
         compute_pass<LPR, CPL>(A, xp, xs, y, row_of(p), n, j);
-        if (p + 2 * W < passes) load_pass<LPR, CPL>(A, packed, scales, mins, clamp(row_of(p + 2 * W)), k, j);
+        if (p + 2 * W < passes)
+            load_pass<LPR, CPL, RAGGED>(A, packed, scales, mins, clamp(row_of(p + 2 * W)), k, j);
         p += W;
         if (p >= passes) break;
         compute_pass<LPR, CPL>(B, xp, xs, y, row_of(p), n, j);
-        if (p + 2 * W < passes) load_pass<LPR, CPL>(B, packed, scales, mins, clamp(row_of(p + 2 * W)), k, j);
+        if (p + 2 * W < passes)
+            load_pass<LPR, CPL, RAGGED>(B, packed, scales, mins, clamp(row_of(p + 2 * W)), k, j);
         p += W;
     }
 }
@@ -328,7 +359,7 @@ gemm_batched_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
     const int wave = tid >> 6;
     const int j = lane % LPR;
     const int rsub = lane / LPR;
-    const int CPL = C / LPR;
+    const int CPL = (C + LPR - 1) / LPR;  // ragged rows: lanes skip chunks past C
     const long passes = ((long)n + RPW - 1) / RPW;
     const long p0 = ((long)blockIdx.x * (blockDim.x >> 6) + wave) * (long)ppw;
 
@@ -344,6 +375,7 @@ gemm_batched_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
         for (int b = 0; b < BT; ++b) yl[b] = 0.0f;
         for (int t = 0; t < CPL; ++t) {
             const int c = j + t * LPR;
+            if (c >= C) break;
             const u4 q = __builtin_nontemporal_load(rp + c);
             const uint16_t s = scales[gbase + (c >> 2)];
             const uint16_t m = mins[gbase + (c >> 2)];
@@ -381,11 +413,12 @@ int lanes_per_row(int k) {
     if (C % 64 == 0) return 64;
     if (C % 32 == 0) return 32;
     if (C % 16 == 0) return 16;
+    if (C > 64) return 64;  // ragged: 8 or 4 lanes per row would leave most CUs idle
     if (C % 8 == 0) return 8;
     return 4;  // C = 4 * (K / 128) is always a multiple of 4
 }
 
-template <int LPR, int CPL>
+template <int LPR, int CPL, bool RAGGED>
 static hipError_t launch_reg(const GemvArgs& a, const DeviceInfo& dev, hipStream_t st) {
     constexpr int RPW = 64 / LPR;
     constexpr int kThreads = kGemvThreads;
@@ -396,7 +429,7 @@ static hipError_t launch_reg(const GemvArgs& a, const DeviceInfo& dev, hipStream
     if (per_cu == 0) {
         int nb = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &nb, reinterpret_cast<const void*>(&gemv_reg_kernel<LPR, CPL>), kThreads, 8192 * 2);
+            &nb, reinterpret_cast<const void*>(&gemv_reg_kernel<LPR, CPL, RAGGED>), kThreads, 8192 * 2);
         if (e != hipSuccess) return e;
         per_cu = nb > 0 ? nb : 1;
     }
@@ -404,22 +437,27 @@ static hipError_t launch_reg(const GemvArgs& a, const DeviceInfo& dev, hipStream
     long grid = (long)dev.num_cu * per_cu;
     const long need = (passes + (kThreads / 64) - 1) / (kThreads / 64);
     if (grid > need) grid = need;
-    hipLaunchKernelGGL((gemv_reg_kernel<LPR, CPL>), dim3((unsigned)grid), dim3(kThreads), lds, st,
+    hipLaunchKernelGGL((gemv_reg_kernel<LPR, CPL, RAGGED>), dim3((unsigned)grid), dim3(kThreads), lds, st,
                        a.packed, a.scales, a.mins, a.x, a.y, a.n, a.k);
     return hipGetLastError();
 }
 
 // Returns hipErrorNotSupported when (LPR, CPL) has no register-resident
 // instantiation; the caller then uses the batched kernel with one column.
-static hipError_t dispatch_reg(int lpr, int cpl, const GemvArgs& a, const DeviceInfo& dev, hipStream_t st) {
+static hipError_t dispatch_reg(int lpr, int cpl, bool ragged, const GemvArgs& a, const DeviceInfo& dev,
+                               hipStream_t st) {
 #define Q4_REG(L, P) \
-    if (lpr == L && cpl == P) return launch_reg<L, P>(a, dev, st);
+    if (!ragged && lpr == L && cpl == P) return launch_reg<L, P, false>(a, dev, st);
+#define Q4_REG_R(L, P) \
+    if (ragged && lpr == L && cpl == P) return launch_reg<L, P, true>(a, dev, st);
     Q4_REG(64, 1) Q4_REG(64, 2) Q4_REG(64, 3) Q4_REG(64, 4)
     Q4_REG(32, 1) Q4_REG(32, 3)
     Q4_REG(16, 1) Q4_REG(16, 3)
     Q4_REG(8, 1) Q4_REG(8, 3)
     Q4_REG(4, 1) Q4_REG(4, 3)
+    Q4_REG_R(64, 2) Q4_REG_R(64, 3) Q4_REG_R(64, 4) Q4_REG_R(64, 5) Q4_REG_R(64, 6)
 #undef Q4_REG
+#undef Q4_REG_R
     return hipErrorNotSupported;
 }
 
@@ -535,8 +573,9 @@ static int max_cols_per_launch(int k, const DeviceInfo& dev) {
 
 hipError_t launch_gemv(const GemvArgs& a, const DeviceInfo& dev, hipStream_t st) {
     const int lpr = lanes_per_row(a.k);
-    const int cpl = (a.k >> 5) / lpr;
-    hipError_t e = dispatch_reg(lpr, cpl, a, dev, st);
+    const int C = a.k >> 5;
+    const int cpl = (C + lpr - 1) / lpr;
+    hipError_t e = dispatch_reg(lpr, cpl, C % lpr != 0, a, dev, st);
     if (e != hipErrorNotSupported) return e;
     return dispatch_batched(lpr, 1, a, a.x, a.y, 1, dev, st);
 }
@@ -550,13 +589,16 @@ hipError_t launch_small_batch(const GemvArgs& a, const uint16_t* X, float* Y, in
         return launch_gemv(one, dev, st);
     }
     const int lpr = lanes_per_row(a.k);
+    const int C = a.k >> 5;
+    const bool ragged = C % lpr != 0;
     const int cap = max_cols_per_launch(a.k, dev);
     for (int b0 = 0; b0 < b; b0 += cap) {
         const int nb = (b - b0) < cap ? (b - b0) : cap;
         const int bt = round_up_pow2_batch(nb);
         const uint16_t* Xc = X + (size_t)b0 * (size_t)a.k;
         float* Yc = Y + (size_t)b0 * (size_t)a.n;
-        hipError_t e = dispatch_cols(lpr, (a.k >> 5) / lpr, bt, a, Xc, Yc, nb, dev, st);
+        // The columns kernel has no ragged rows; those go to the batched kernel.
+        hipError_t e = ragged ? hipErrorNotSupported : dispatch_cols(lpr, C / lpr, bt, a, Xc, Yc, nb, dev, st);
         if (e == hipErrorNotSupported) e = dispatch_batched(lpr, bt, a, Xc, Yc, nb, dev, st);
         if (e != hipSuccess) return e;
     }

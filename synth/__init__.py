@@ -104,6 +104,11 @@ FUSED_N, HIDDEN_K = 25088, 3072
 OPROJ_N, OPROJ_K = 3072, 3072
 DOWN_N, DOWN_K = 3072, 8192
 STACK_LAYERS = 36
+# The pages' own model (rumik-oss-1) appears to have hidden size 2,048: the
+# fused projection keeps its 25,088 rows, o_proj is 2,048 x 2,048 and down is
+# 2,048 x 11,008 (a reconstruction from the pages' per-token byte counts).
+PAGES_HIDDEN = 2048
+PAGES_FFN = 11008
 
 SEEDS = {
     "tiny": 0,
@@ -114,6 +119,9 @@ SEEDS = {
     "prefill_x34": 5,
     "prefill_x256": 6,
     "float_weights": 21,
+    "pages_fused": 11,
+    "pages_oproj": 12,
+    "pages_down": 13,
 }
 
 
@@ -128,6 +136,9 @@ WORKLOADS = {
     "fused_25088x3072": (FUSED_N, HIDDEN_K, SEEDS["fused"]),
     "oproj_3072x3072": (OPROJ_N, OPROJ_K, SEEDS["oproj"]),
     "down_3072x8192": (DOWN_N, DOWN_K, SEEDS["down"]),
+    "pages_fused_25088x2048": (FUSED_N, PAGES_HIDDEN, SEEDS["pages_fused"]),
+    "pages_oproj_2048x2048": (PAGES_HIDDEN, PAGES_HIDDEN, SEEDS["pages_oproj"]),
+    "pages_down_2048x11008": (PAGES_HIDDEN, PAGES_FFN, SEEDS["pages_down"]),
 }
 
 

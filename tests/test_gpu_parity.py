@@ -97,6 +97,9 @@ def test_dyadic_bit_exact(dev, n, k):
 SHAPES = [
     (1, 128), (2, 256), (3, 384), (17, 512), (33, 640), (255, 768), (64, 1024), (5, 1152),
     (1000, 2048), (129, 3072), (31, 4096), (7, 6144), (300, 8192), (19, 11008), (3, 16384), (2, 32768),
+    # ragged rows (K not a multiple of 512 and above 2,048): 64 lanes per row,
+    # the last chunk column partial; 6 and 7 chunks per lane take the two paths
+    (70, 2176), (40, 6400), (33, 12160), (20, 12416), (7, 32640), (2048, 11008),
 ]
 
 
@@ -111,7 +114,8 @@ def test_gemv_parity_shapes(dev, n, k):
     assert_bound(y, ref, gemv_bound(packed_np, w, x)[0], 128, f"gemv {n}x{k}")
 
 
-@pytest.mark.parametrize("name", ["tiny_256x512", "fused_25088x3072", "oproj_3072x3072", "down_3072x8192"])
+@pytest.mark.parametrize("name", ["tiny_256x512", "fused_25088x3072", "oproj_3072x3072", "down_3072x8192",
+                                  "pages_fused_25088x2048", "pages_oproj_2048x2048", "pages_down_2048x11008"])
 def test_gemv_parity_workloads(dev, name):
     w, x = synth.workload(name)
     packed_np = oracle.pack(w.codes)
@@ -137,7 +141,8 @@ def test_gemv_zero_and_scaling(dev):
 # batch: bit-identity with the batch-1 call, and parity
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("n,k", [(25088, 3072), (3072, 8192), (257, 512), (100, 11008), (33, 384), (9, 32768)])
+@pytest.mark.parametrize("n,k", [(25088, 3072), (3072, 8192), (257, 512), (100, 11008), (33, 384), (9, 32768),
+                                 (2048, 11008), (300, 2176), (64, 12160), (50, 12416)])
 def test_small_batch_bit_identical_to_gemv(dev, n, k):
     w = synth.weights(n, k, seed=n + k)
     packed, s, m = upload(w, dev, q4)
