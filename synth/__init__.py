@@ -76,6 +76,22 @@ def float_weights(n: int, k: int, seed: int) -> np.ndarray:
     return draw_float_weights(_rng(seed), n, k)
 
 
+def draw_head_int8(rng: np.random.Generator, n: int, k: int):
+    """int8 output-head weights: codes uniform on -127..127 (the symmetric
+    range), one fp16 scale per row uniform on [0.0005, 0.01]."""
+    q = rng.integers(-127, 128, (n, k), dtype=np.int8)
+    s = rng.uniform(0.0005, 0.01, n).astype(np.float16)
+    return q, s
+
+
+def head_int8_case(n: int, k: int, seed: int):
+    """(q, scales, x) of one int8 head from one generator."""
+    rng = _rng(seed)
+    q, s = draw_head_int8(rng, n, k)
+    x = draw_activations(rng, 1, k)[0]
+    return q, s, x
+
+
 def draw_activations(rng: np.random.Generator, b: int, k: int) -> np.ndarray:
     return rng.standard_normal((b, k)).astype(np.float16)
 
@@ -122,7 +138,11 @@ SEEDS = {
     "pages_fused": 11,
     "pages_oproj": 12,
     "pages_down": 13,
+    "head_int8": 31,
 }
+# int8 output head: 16,384 rows (an assumed audio vocabulary of 8 codebooks x
+# 2,048 entries; the pages give no head size) by the hidden size.
+HEAD_N = 16384
 
 
 def stack_seed(layer: int, which: int) -> int:
