@@ -10,8 +10,8 @@ same launches replayed from a HIP graph are timed as a cross-check that must
 reproduce the eager output.
 
 Prints ONE JSON line.  Extra forms (other shapes, small batch, prompt
-processing, the export quantiser, the 36-layer stack) are reported under
-"forms".
+processing, the int8 output head, the export quantiser, the pages' 108-launch
+step and the 36-layer stack) are reported under "forms".
 """
 from __future__ import annotations
 
@@ -184,6 +184,25 @@ def quantize_launcher(q4, Ws, packed, scales, mins, n, k):
 
     def launch(i, st):
         rc = lib.q4g128_quantize(ptrs[i % R], pp, sp, mp, n, k, st)
+        if rc != 0:
+            raise RuntimeError(q4.q4g128_status_string(rc))
+    return launch
+
+
+def head_bytes(n: int, k: int) -> int:
+    """int8 codes + fp16 row scales + fp16 activations read."""
+    return n * k + 2 * n + 2 * k
+
+
+def head_launcher(q4, sets, x, y, n, k):
+    lib = q4.library()
+    ptrs = [(qq.data_ptr(), ss.data_ptr()) for qq, ss in sets]
+    xp, yp = x.data_ptr(), y.data_ptr()
+    R = len(ptrs)
+
+    def launch(i, st):
+        qq, ss = ptrs[i % R]
+        rc = lib.q4g128_gemv_int8(qq, ss, xp, yp, n, k, st)
         if rc != 0:
             raise RuntimeError(q4.q4g128_status_string(rc))
     return launch
@@ -372,6 +391,20 @@ def main():
                 "frac_mfma_f16": round(flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
         del rot
         torch.cuda.empty_cache()
+        # int8 output head, 16,384 x 3,072
+        hn, hk = synth.HEAD_N, synth.HIDDEN_K
+        hq, hs, hx = synth.head_int8_case(hn, hk, synth.SEEDS["head_int8"])
+        hq_d, hs_d = torch.from_numpy(hq).to(dev), f16(hs)
+        hsets = [(hq_d, hs_d)] + [(hq_d.clone(), hs_d.clone())
+                                  for _ in range(max(0, -(-MALL_DEFEAT_BYTES // head_bytes(hn, hk)) - 1))]
+        hy = torch.empty(hn, dtype=torch.float32, device=dev)
+        ms = time_checked(torch, stream, head_launcher(q4, hsets, f16(hx), hy, hn, hk), hy, 1000, 20, GRAPH_LAUNCHES)
+        hb = head_bytes(hn, hk)
+        forms["head_int8_16384x3072_gemv_b1"] = {
+            "us_per_call": round(ms * 1e3, 3), "GB_per_s": round(hb / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(hb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "copies_rotated": len(hsets),
+            "bytes_per_call": hb}
+        del hsets, hq_d, hs_d, hy
         # export quantiser on the fused projection's float32 weights
         Wf = torch.from_numpy(synth.float_weights(n, k, synth.SEEDS["float_weights"])).to(dev)
         Ws = [Wf] + [Wf.clone() for _ in range(max(0, -(-MALL_DEFEAT_BYTES // (n * k * 4)) - 1))]

@@ -68,6 +68,7 @@ typedef int32_t q4_status;
 #define Q4G128_MAX_K 32768
 #define Q4G128_MAX_BATCH 16
 #define Q4G128_MAX_N 0x7FFFFF00LL
+#define Q4G128_INT8_MAX_K 8192
 
 /*
  * q4g128_pack -- two codes per byte.
@@ -143,6 +144,25 @@ Q4_API q4_status q4g128_gemm_small_batch(const uint8_t* packed, const uint16_t* 
 Q4_API q4_status q4g128_gemm_prefill(const uint8_t* packed, const uint16_t* scales,
                               const uint16_t* mins, const uint16_t* X, float* Y,
                               int64_t n, int64_t k, int64_t m, void* stream);
+
+/*
+ * q4g128_gemv_int8 -- y[n] = scale[n] * sum_k q[n][k] * x[k]  (int8 output head).
+ * The rumik write-up moved the audio output head to int8 with a kernel of its
+ * own: int4 group-128 was measurably too lossy there (the passage on the
+ * remaining per-token time after the 36 layers, and "What I would tell
+ * someone starting this").  The pages give no int8 layout; the reading
+ * implemented is per-row symmetric int8:
+ *   q      [N][K] int8, row-major, every value -128..127 accepted;
+ *   scales [N] fp16 bit patterns, one per output row;
+ *   x      [K] fp16;  y [N] fp32, written in full.
+ * Products q*x are exact; sums are fp32 in a fixed order (deterministic).
+ * Errors: Q4_EINVAL for a NULL pointer, N <= 0 or y overlapping an input;
+ * Q4_ESHAPE unless K is a multiple of 128 with 128 <= K <= 8192 and
+ * N <= Q4G128_MAX_N; Q4_EALIGN unless q and x are 16-byte, scales 2-byte
+ * and y 4-byte aligned; Q4_EDEVICE as for the other entry points.
+ */
+Q4_API q4_status q4g128_gemv_int8(const int8_t* q, const uint16_t* scales, const uint16_t* x,
+                           float* y, int64_t n, int64_t k, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 Q4_API const char* q4g128_status_string(q4_status status);

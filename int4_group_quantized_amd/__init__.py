@@ -29,6 +29,7 @@ Q4_EDEVICE = -4
 GROUP = 128
 MAX_K = 32768
 MAX_BATCH = 16
+INT8_MAX_K = 8192
 
 EXPORTED = (
     "q4g128_pack",
@@ -36,6 +37,7 @@ EXPORTED = (
     "q4g128_gemv",
     "q4g128_gemm_small_batch",
     "q4g128_gemm_prefill",
+    "q4g128_gemv_int8",
     "q4g128_status_string",
     "q4g128_last_hip_error",
 )
@@ -63,7 +65,9 @@ def _load():
     lib.q4g128_gemv.argtypes = [vp, vp, vp, vp, vp, i64, i64, vp]
     lib.q4g128_gemm_small_batch.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.q4g128_gemm_prefill.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
-    for name in ("q4g128_pack", "q4g128_quantize", "q4g128_gemv", "q4g128_gemm_small_batch", "q4g128_gemm_prefill"):
+    lib.q4g128_gemv_int8.argtypes = [vp, vp, vp, vp, i64, i64, vp]
+    for name in ("q4g128_pack", "q4g128_quantize", "q4g128_gemv", "q4g128_gemm_small_batch", "q4g128_gemm_prefill",
+                 "q4g128_gemv_int8"):
         getattr(lib, name).restype = ctypes.c_int32
     lib.q4g128_status_string.argtypes = [ctypes.c_int32]
     lib.q4g128_status_string.restype = ctypes.c_char_p
@@ -208,6 +212,24 @@ def q4g128_gemm_prefill(packed, scales, mins, X, Y=None, stream=None) -> torch.T
                                         X.data_ptr(), Y.data_ptr(), n, k, m, _stream(dev, stream)),
                "q4g128_gemm_prefill")
     return Y
+
+
+def q4g128_gemv_int8(q, scales, x, y=None, stream=None) -> torch.Tensor:
+    """y[N] fp32 = scale[n] * (q x) for int8 q [N][K], fp16 scales [N], fp16 x [K]."""
+    if q.dim() != 2:
+        raise ValueError("q must be [N][K]")
+    n, k = q.shape
+    _dev_tensor(q, "q", torch.int8, (n, k))
+    _dev_tensor(scales, "scales", torch.float16, (n,))
+    _dev_tensor(x, "x", torch.float16, (k,))
+    if y is None:
+        y = torch.empty((n,), dtype=torch.float32, device=q.device)
+    _dev_tensor(y, "y", torch.float32, (n,))
+    dev = _same_device(q, scales, x, y)
+    with torch.cuda.device(dev):
+        _check(_lib.q4g128_gemv_int8(q.data_ptr(), scales.data_ptr(), x.data_ptr(), y.data_ptr(), n, k,
+                                     _stream(dev, stream)), "q4g128_gemv_int8")
+    return y
 
 
 def q4g128_status_string(status: int) -> str:

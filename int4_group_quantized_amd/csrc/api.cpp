@@ -166,6 +166,23 @@ q4_status q4g128_gemm_prefill(const uint8_t* packed, const uint16_t* scales, con
     return e == hipSuccess ? Q4_OK : device_error(e);
 }
 
+q4_status q4g128_gemv_int8(const int8_t* q, const uint16_t* scales, const uint16_t* x, float* y, int64_t n,
+                           int64_t k, void* stream) {
+    if (!q || !scales || !x || !y) return Q4_EINVAL;
+    if (n <= 0) return Q4_EINVAL;
+    if (k < Q4G128_GROUP || k % Q4G128_GROUP != 0 || k > Q4G128_INT8_MAX_K || n > Q4G128_MAX_N) return Q4_ESHAPE;
+    if (!aligned(q, 16) || !aligned(x, 16) || !aligned(scales, 2) || !aligned(y, 4)) return Q4_EALIGN;
+    const size_t ybytes = (size_t)n * sizeof(float);
+    if (overlaps(y, ybytes, q, (size_t)n * (size_t)k) || overlaps(y, ybytes, scales, (size_t)n * 2) ||
+        overlaps(y, ybytes, x, (size_t)k * 2))
+        return Q4_EINVAL;
+    q4::DeviceInfo dev;
+    q4_status s = current_device(&dev);
+    if (s != Q4_OK) return s;
+    hipError_t e = q4::launch_head_int8(q, scales, x, y, n, k, dev, (hipStream_t)stream);
+    return e == hipSuccess ? Q4_OK : device_error(e);
+}
+
 const char* q4g128_status_string(q4_status status) {
     switch (status) {
         case Q4_OK: return "Q4_OK: success";

@@ -69,6 +69,10 @@ def quantize(w=X, p=P, s=S, m=M, n=64, k=256):
     return q4.library().q4g128_quantize(w, p, s, m, n, k, None)
 
 
+def head(qq=P, s=S, x=X, y=Y, n=64, k=256):
+    return q4.library().q4g128_gemv_int8(qq, s, x, y, n, k, None)
+
+
 @pytest.mark.parametrize("call", [
     lambda: gemv(p=None), lambda: gemv(s=None), lambda: gemv(m=None), lambda: gemv(x=None),
     lambda: gemv(y=None), lambda: gemv(n=0), lambda: gemv(n=-5),
@@ -77,6 +81,7 @@ def quantize(w=X, p=P, s=S, m=M, n=64, k=256):
     lambda: pack(c=None), lambda: pack(p=None), lambda: pack(n=0),
     lambda: quantize(w=None), lambda: quantize(p=None), lambda: quantize(s=None), lambda: quantize(m=None),
     lambda: quantize(n=0), lambda: quantize(n=-2),
+    lambda: head(qq=None), lambda: head(s=None), lambda: head(x=None), lambda: head(y=None), lambda: head(n=0),
 ])
 def test_einval(call):
     assert call() == EINVAL
@@ -90,6 +95,7 @@ def test_eshape_k(k):
     assert prefill(5, k=k) == expect
     assert pack(k=k) == expect
     assert quantize(k=k) == expect
+    assert head(k=k) == expect
 
 
 def test_eshape_sizes():
@@ -98,6 +104,18 @@ def test_eshape_sizes():
     assert quantize(n=1 << 31) == ESHAPE
     # more groups than the export kernel's grid covers: N * K/128 > 2^36
     assert quantize(n=(1 << 31) - 256, k=32768) == ESHAPE
+
+
+def test_head_int8_limits():
+    assert head(k=8192 + 128) == ESHAPE  # int8 head rows are at most 8,192 codes
+    assert head(n=1 << 31) == ESHAPE
+    assert head(qq=P + 8) == EALIGN
+    assert head(x=X + 2) == EALIGN
+    assert head(s=S + 1) == EALIGN
+    assert head(y=Y + 2) == EALIGN
+    assert head(y=P + 64) == EINVAL   # y inside q
+    assert head(y=X) == EINVAL        # y on x
+    assert head(y=S + 4) == EINVAL    # y inside scales
 
 
 @pytest.mark.parametrize("which", ["w", "p", "s", "m"])
