@@ -81,6 +81,22 @@ Q4_API q4_status q4g128_pack(const uint8_t* codes, uint8_t* packed,
                       int64_t n, int64_t k, void* stream);
 
 /*
+ * q4g128_gemm_prefill_epilogue -- the same Y[m][n] = sum_k w[n][k] * X[m][k]
+ * in the form of the rumik write-up's prefill ("Step 8: a prefill that
+ * stays int4"): each 128-column group is unpacked on chip to exact integer
+ * codes and contracted with the activations on the matrix cores (fp32
+ * accumulation), and the group's scale and minimum are applied to that
+ * result: Y += scale * sum(code*x) + min * sum(x).  No weight is rounded to
+ * fp16, so results carry only fp32 summation error (within 512 * 2^-24 *
+ * sum_k |w*x| of the exact product).  Same arguments, limits, errors and
+ * execution model as q4g128_gemm_prefill; any M >= 1 (blocks of 64 tokens
+ * re-read the weights).
+ */
+Q4_API q4_status q4g128_gemm_prefill_epilogue(const uint8_t* packed, const uint16_t* scales,
+                                       const uint16_t* mins, const uint16_t* X, float* Y,
+                                       int64_t n, int64_t k, int64_t m, void* stream);
+
+/*
  * q4g128_quantize -- export float32 weights to the format above.
  * The rumik write-up ("Step 3") exports every projection with a short CPU
  * job: groups of 128 columns, one fp16 scale and one fp16 minimum per group.

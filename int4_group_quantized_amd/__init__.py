@@ -37,6 +37,7 @@ EXPORTED = (
     "q4g128_gemv",
     "q4g128_gemm_small_batch",
     "q4g128_gemm_prefill",
+    "q4g128_gemm_prefill_epilogue",
     "q4g128_gemv_int8",
     "q4g128_status_string",
     "q4g128_last_hip_error",
@@ -66,8 +67,9 @@ def _load():
     lib.q4g128_gemm_small_batch.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.q4g128_gemm_prefill.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.q4g128_gemv_int8.argtypes = [vp, vp, vp, vp, i64, i64, vp]
+    lib.q4g128_gemm_prefill_epilogue.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
     for name in ("q4g128_pack", "q4g128_quantize", "q4g128_gemv", "q4g128_gemm_small_batch", "q4g128_gemm_prefill",
-                 "q4g128_gemv_int8"):
+                 "q4g128_gemv_int8", "q4g128_gemm_prefill_epilogue"):
         getattr(lib, name).restype = ctypes.c_int32
     lib.q4g128_status_string.argtypes = [ctypes.c_int32]
     lib.q4g128_status_string.restype = ctypes.c_char_p
@@ -211,6 +213,24 @@ def q4g128_gemm_prefill(packed, scales, mins, X, Y=None, stream=None) -> torch.T
         _check(_lib.q4g128_gemm_prefill(packed.data_ptr(), scales.data_ptr(), mins.data_ptr(),
                                         X.data_ptr(), Y.data_ptr(), n, k, m, _stream(dev, stream)),
                "q4g128_gemm_prefill")
+    return Y
+
+
+def q4g128_gemm_prefill_epilogue(packed, scales, mins, X, Y=None, stream=None) -> torch.Tensor:
+    """Y[M][N] fp32 = X W^T for fp16 X [M][K]: exact codes on the matrix cores, scale and min per group on the result."""
+    n, k = _weights(packed, scales, mins)
+    if X.dim() != 2:
+        raise ValueError("X must be [M][K]")
+    m = X.shape[0]
+    _dev_tensor(X, "X", torch.float16, (m, k))
+    if Y is None:
+        Y = torch.empty((m, n), dtype=torch.float32, device=packed.device)
+    _dev_tensor(Y, "Y", torch.float32, (m, n))
+    dev = _same_device(packed, scales, mins, X, Y)
+    with torch.cuda.device(dev):
+        _check(_lib.q4g128_gemm_prefill_epilogue(packed.data_ptr(), scales.data_ptr(), mins.data_ptr(),
+                                                 X.data_ptr(), Y.data_ptr(), n, k, m, _stream(dev, stream)),
+               "q4g128_gemm_prefill_epilogue")
     return Y
 
 

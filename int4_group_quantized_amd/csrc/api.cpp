@@ -166,6 +166,21 @@ q4_status q4g128_gemm_prefill(const uint8_t* packed, const uint16_t* scales, con
     return e == hipSuccess ? Q4_OK : device_error(e);
 }
 
+q4_status q4g128_gemm_prefill_epilogue(const uint8_t* packed, const uint16_t* scales, const uint16_t* mins,
+                                       const uint16_t* X, float* Y, int64_t n, int64_t k, int64_t m,
+                                       void* stream) {
+    if (m < 1) return Q4_EINVAL;
+    q4_status s = check_product(packed, scales, mins, X, Y, n, k, m);
+    if (s != Q4_OK) return s;
+    if ((size_t)m * (size_t)n > (size_t)0x7FFFFFFFFFFFLL) return Q4_ESHAPE;
+    q4::DeviceInfo dev;
+    s = current_device(&dev);
+    if (s != Q4_OK) return s;
+    hipError_t e = q4::launch_prefill_epilogue(make_args(packed, scales, mins, X, Y, n, k), X, Y, (int)m, dev,
+                                               (hipStream_t)stream);
+    return e == hipSuccess ? Q4_OK : device_error(e);
+}
+
 q4_status q4g128_gemv_int8(const int8_t* q, const uint16_t* scales, const uint16_t* x, float* y, int64_t n,
                            int64_t k, void* stream) {
     if (!q || !scales || !x || !y) return Q4_EINVAL;

@@ -34,14 +34,6 @@ namespace q4 {
 constexpr int kPrefillWaves = 8;
 constexpr int kPrefillRowsPerBlock = 16 * kPrefillWaves;
 
-// Workgroup barrier for LDS hand-offs only.  It waits for this wave's LDS
-// operations and does not drain outstanding global loads (unlike
-// __syncthreads, whose fence would empty the prefetch rings).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
-    __builtin_amdgcn_s_barrier();
-}
-
 // fp16 weights of one chunk (packed codes q, scale and minimum of its
 // group), 16 pairs in the permuted pair order.
 __device__ __forceinline__ void weights_fp16(const u4 q, uint16_t sb, uint16_t mb, const DequantConsts& kc,

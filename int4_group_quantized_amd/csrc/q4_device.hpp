@@ -155,6 +155,14 @@ __device__ __forceinline__ void dequant_dword(uint32_t q, const DequantConsts& k
     out[3] = __builtin_elementwise_fma(as_h2(d), sixteenth, neg64);
 }
 
+// Workgroup barrier for LDS hand-offs only.  It waits for this wave's LDS
+// operations and does not drain outstanding global loads (unlike
+// __syncthreads, whose fence would empty the prefetch rings).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
+    __builtin_amdgcn_s_barrier();
+}
+
 // One group-slice update of a lane's running row sum (all in 2^-20 units):
 //   y += scale * sum(code*x) ; y += min * sum(x)
 // i.e. sum((code*scale + min) * x) over the slice, with each term once.

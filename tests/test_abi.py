@@ -61,6 +61,10 @@ def prefill(mm, p=P, s=S, m=M, x=X, y=Y, n=64, k=256):
     return q4.library().q4g128_gemm_prefill(p, s, m, x, y, n, k, mm, None)
 
 
+def prefill_epi(mm, p=P, s=S, m=M, x=X, y=Y, n=64, k=256):
+    return q4.library().q4g128_gemm_prefill_epilogue(p, s, m, x, y, n, k, mm, None)
+
+
 def pack(c=X, p=P, n=64, k=256):
     return q4.library().q4g128_pack(c, p, n, k, None)
 
@@ -78,6 +82,7 @@ def head(qq=P, s=S, x=X, y=Y, n=64, k=256):
     lambda: gemv(y=None), lambda: gemv(n=0), lambda: gemv(n=-5),
     lambda: batch(0), lambda: batch(17), lambda: batch(-1), lambda: batch(4, x=None),
     lambda: prefill(0), lambda: prefill(-3), lambda: prefill(34, y=None),
+    lambda: prefill_epi(0), lambda: prefill_epi(34, p=None), lambda: prefill_epi(34, y=M),
     lambda: pack(c=None), lambda: pack(p=None), lambda: pack(n=0),
     lambda: quantize(w=None), lambda: quantize(p=None), lambda: quantize(s=None), lambda: quantize(m=None),
     lambda: quantize(n=0), lambda: quantize(n=-2),
@@ -93,6 +98,7 @@ def test_eshape_k(k):
     assert gemv(k=k) == expect
     assert batch(3, k=k) == expect
     assert prefill(5, k=k) == expect
+    assert prefill_epi(5, k=k) == expect
     assert pack(k=k) == expect
     assert quantize(k=k) == expect
     assert head(k=k) == expect
@@ -138,6 +144,7 @@ def test_ealign(which):
     assert gemv(**{which: bad}) == EALIGN
     assert batch(2, **{which: bad}) == EALIGN
     assert prefill(20, **{which: bad}) == EALIGN
+    assert prefill_epi(20, **{which: bad}) == EALIGN
 
 
 def test_alignment_minimums_accepted_by_validation_order():
