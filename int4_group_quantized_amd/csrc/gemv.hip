@@ -32,13 +32,6 @@ namespace q4 {
 // are requested before the activations are staged.
 // ---------------------------------------------------------------------------
 
-// Rank of workgroup b among the workgroups of its XCD, laid out XCD by XCD.
-__device__ __forceinline__ int xcd_block_order(int b, int grid) {
-    constexpr int kXcd = 8;
-    const int per = grid / kXcd, rem = grid % kXcd, x = b % kXcd;
-    return x * per + (x < rem ? x : rem) + b / kXcd;
-}
-
 template <int CPL>
 struct PassLoad {
     u4 q[CPL];

@@ -29,12 +29,6 @@ namespace q4 {
 
 constexpr int kHeadThreads = 512;
 
-__device__ __forceinline__ int head_xcd_order(int b, int grid) {
-    constexpr int kXcd = 8;
-    const int per = grid / kXcd, rem = grid % kXcd, x = b % kXcd;
-    return x * per + (x < rem ? x : rem) + b / kXcd;
-}
-
 template <int CPL>
 struct HeadRow {
     u4 q[CPL];
@@ -95,7 +89,7 @@ head_int8_kernel(const int8_t* __restrict__ q, const uint16_t* __restrict__ scal
     const int j = tid & 63;
     const int wave = tid >> 6;
     const long W = (long)gridDim.x * (blockDim.x >> 6);
-    long p = (long)wave * gridDim.x + head_xcd_order(blockIdx.x, gridDim.x);
+    long p = (long)wave * gridDim.x + xcd_block_order(blockIdx.x, gridDim.x);
     auto clamp = [&](long r) { return (int)(r < n ? r : n - 1); };
 
     HeadRow<CPL> A, B;

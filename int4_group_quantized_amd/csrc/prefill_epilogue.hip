@@ -34,20 +34,6 @@ namespace q4 {
 constexpr int kEpiWaves = 8;
 constexpr int kEpiRowsPerBlock = 16 * kEpiWaves;
 
-template <int CTRL>
-__device__ __forceinline__ float epi_dpp(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over the 16 lanes of a DPP row; every lane of the row gets the sum.
-__device__ __forceinline__ float row16_sum(float v) {
-    v = v + epi_dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-    v = v + epi_dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-    v = v + epi_dpp<0x141>(v);  // row_half_mirror
-    v = v + epi_dpp<0x140>(v);  // row_mirror
-    return v;
-}
-
 template <int TT>
 __global__ void __launch_bounds__(64 * kEpiWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_epilogue_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
@@ -113,7 +99,7 @@ prefill_epilogue_kernel(const uint8_t* __restrict__ packed, const uint16_t* __re
                 part = __builtin_amdgcn_fdot2(as_h2(v.y), ones, part, false);
                 part = __builtin_amdgcn_fdot2(as_h2(v.z), ones, part, false);
                 part = __builtin_amdgcn_fdot2(as_h2(v.w), ones, part, false);
-                const float tot = row16_sum(part);
+                const float tot = reduce_lanes<16>(part);  // every lane of the DPP row gets the token's sum
                 if (w < WIN) {
                     xt[buf][w >> 4][w & 15] = v;
                     if ((w & 15) == 0) reinterpret_cast<float*>(&xs[buf][0])[w >> 4] = tot;

@@ -155,6 +155,15 @@ __device__ __forceinline__ void dequant_dword(uint32_t q, const DequantConsts& k
     out[3] = __builtin_elementwise_fma(as_h2(d), sixteenth, neg64);
 }
 
+// Rank of workgroup b among the workgroups of its XCD, laid out XCD by XCD
+// (the dispatcher deals workgroups to the 8 XCDs round-robin, block b on
+// XCD b % 8): consecutive ranks then share one L2.
+__device__ __forceinline__ int xcd_block_order(int b, int grid) {
+    constexpr int kXcd = 8;
+    const int per = grid / kXcd, rem = grid % kXcd, x = b % kXcd;
+    return x * per + (x < rem ? x : rem) + b / kXcd;
+}
+
 // Workgroup barrier for LDS hand-offs only.  It waits for this wave's LDS
 // operations and does not drain outstanding global loads (unlike
 // __syncthreads, whose fence would empty the prefetch rings).
@@ -183,14 +192,18 @@ __device__ __forceinline__ float dpp_move(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
+// The value of lane ^ 16 within each 32-lane half.
+__device__ __forceinline__ float lane_swap16(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+
 template <int LPR>
 __device__ __forceinline__ float reduce_lanes(float v) {
     if constexpr (LPR >= 2) v = v + dpp_move<0xB1>(v);    // quad_perm [1,0,3,2]
     if constexpr (LPR >= 4) v = v + dpp_move<0x4E>(v);    // quad_perm [2,3,0,1]
     if constexpr (LPR >= 8) v = v + dpp_move<0x141>(v);   // row_half_mirror
     if constexpr (LPR >= 16) v = v + dpp_move<0x140>(v);  // row_mirror
-    if constexpr (LPR >= 32)
-        v = v + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+    if constexpr (LPR >= 32) v = v + lane_swap16(v);
     if constexpr (LPR >= 64) v = v + __shfl_xor(v, 32, 64);
     return v;
 }

@@ -25,27 +25,18 @@ constexpr int kQuantThreads = 256;
 constexpr int kGroupsPerHalf = 4;
 constexpr int kGroupsPerBlock = (kQuantThreads / 32) * kGroupsPerHalf;
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-
-__device__ __forceinline__ float swap16_f(float v) {  // lane ^ 16 within each 32 lanes
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
-}
-
 // Minimum and maximum over the 32 lanes of a half-wave; every lane gets both.
 __device__ __forceinline__ void minmax32(float& lo, float& hi) {
-    lo = fminf(lo, dpp_f<0xB1>(lo));   // quad_perm [1,0,3,2]
-    hi = fmaxf(hi, dpp_f<0xB1>(hi));
-    lo = fminf(lo, dpp_f<0x4E>(lo));   // quad_perm [2,3,0,1]
-    hi = fmaxf(hi, dpp_f<0x4E>(hi));
-    lo = fminf(lo, dpp_f<0x141>(lo));  // row_half_mirror
-    hi = fmaxf(hi, dpp_f<0x141>(hi));
-    lo = fminf(lo, dpp_f<0x140>(lo));  // row_mirror
-    hi = fmaxf(hi, dpp_f<0x140>(hi));
-    lo = fminf(lo, swap16_f(lo));
-    hi = fmaxf(hi, swap16_f(hi));
+    lo = fminf(lo, dpp_move<0xB1>(lo));   // quad_perm [1,0,3,2]
+    hi = fmaxf(hi, dpp_move<0xB1>(hi));
+    lo = fminf(lo, dpp_move<0x4E>(lo));   // quad_perm [2,3,0,1]
+    hi = fmaxf(hi, dpp_move<0x4E>(hi));
+    lo = fminf(lo, dpp_move<0x141>(lo));  // row_half_mirror
+    hi = fmaxf(hi, dpp_move<0x141>(hi));
+    lo = fminf(lo, dpp_move<0x140>(lo));  // row_mirror
+    hi = fmaxf(hi, dpp_move<0x140>(hi));
+    lo = fminf(lo, lane_swap16(lo));
+    hi = fmaxf(hi, lane_swap16(hi));
 }
 
 __device__ __forceinline__ uint32_t code_of(float w, float mf, float sf) {
