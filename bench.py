@@ -300,7 +300,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the GEMV shards by rows without any exchange; see DESIGN.md)", file=sys.stderr)
+              "(the GEMV shards by rows: each GPU would run the same kernel on its row slice)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -8,7 +8,7 @@ What the pages fix (rumik-oss-1 int4 write-up, rtts.neoandmatrix.me, the
 section on the remaining per-token time after the 36 layers, and "What I
 would tell someone starting this"): int4 group-128 was too lossy for the
 audio output head, which was moved to int8 with its own kernel.  The pages
-give no int8 layout.  The reading taken here (listed in the design doc) is the
+give no int8 layout.  The reading taken here is the
 plain per-row symmetric form:
 
     w[n][k] = q[n][k] * scale[n]      q int8 (all of -128..127 accepted),

@@ -13,7 +13,7 @@ matrix W (N output rows x K input columns) is quantised in groups of 128
 consecutive columns of a row; each group carries one fp16 scale and one fp16
 minimum; two 4-bit codes share a byte.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * the dequantised weight is  w = code * scale + min  (code 0 maps to the
     group minimum, code 15 to min + 15*scale);
   * within a byte the LOW nibble holds the EVEN column, the high nibble the

@@ -8,7 +8,7 @@ What the pages fix (rumik-oss-1 int4 write-up, rtts.neoandmatrix.me,
 section "Step 3: an int4 file and a first kernel on the laptop"): a short CPU
 job quantised every projection in groups of 128 columns with one fp16 scale
 and one fp16 minimum per group, two 4-bit codes per byte.  The pages print no
-formula for the codes.  The reading taken here (listed in the design doc) is the
+formula for the codes.  The reading taken here is the
 plain min/max affine quantiser that matches the dequantisation
 w = code * scale + min:
 
