@@ -108,10 +108,20 @@ def time_graph(torch, stream, launch, n_launch_per_graph, steps, warmup, out=Non
     return ms / (reps * n_launch_per_graph), reps * n_launch_per_graph, g
 
 
-def time_eager(torch, stream, launch, steps, warmup):
+SETTLE_S = 0.1  # continuous load before any timed region (clocks ramp up over ~20 ms)
+
+
+def time_eager(torch, stream, launch, steps, warmup, settle_s=SETTLE_S):
+    """ms per call over `steps` back-to-back launches, after `warmup` untimed
+    launches and at least `settle_s` seconds of continuous launching."""
     with torch.cuda.stream(stream):
-        for i in range(warmup):
+        t0 = time.perf_counter()
+        i = 0
+        while i < warmup or time.perf_counter() - t0 < settle_s:
             launch(i, stream.cuda_stream)
+            i += 1
+            if i % 256 == 0:
+                stream.synchronize()  # keep the queue short so the clock measures GPU time
         stream.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         stop = torch.cuda.Event(enable_timing=True)
@@ -350,6 +360,7 @@ def main():
             "bytes_per_call": nbytes,
             "weight_copies_rotated": rot.copies,
             "timing": "back-to-back launches on one stream, HIP events on the launch stream",
+            "settle_s": SETTLE_S,
         },
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "us_per_call": round(ms_eager * 1e3, 3),
