@@ -13,7 +13,7 @@ namespace {
 
 thread_local int32_t g_last_hip_error = 0;
 
-constexpr int kMaxDevices = 64;
+constexpr int kMaxDevices = q4::kMaxDevices;
 q4::DeviceInfo g_dev[kMaxDevices];
 std::mutex g_dev_mu;
 

@@ -417,14 +417,16 @@ static hipError_t launch_reg(const GemvArgs& a, const DeviceInfo& dev, hipStream
     constexpr int kThreads = kGemvThreads;
     const size_t lds = (size_t)a.k * 2;
     // Resident workgroups per CU for this instantiation (registers bound it;
-    // the LDS footprint is at most 16 KB).  Queried once per process.
-    static int per_cu = 0;
+    // the LDS footprint is at most 16 KB).  Queried once per device.
+    std::atomic<int>& cached = PerDevice<&gemv_reg_kernel<LPR, CPL, RAGGED>>::value[dev.device];
+    int per_cu = cached.load(std::memory_order_relaxed);
     if (per_cu == 0) {
         int nb = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &nb, reinterpret_cast<const void*>(&gemv_reg_kernel<LPR, CPL, RAGGED>), kThreads, 8192 * 2);
         if (e != hipSuccess) return e;
         per_cu = nb > 0 ? nb : 1;
+        cached.store(per_cu, std::memory_order_relaxed);
     }
     const long passes = ((long)a.n + RPW - 1) / RPW;
     long grid = (long)dev.num_cu * per_cu;
@@ -460,12 +462,13 @@ static hipError_t launch_batched(const GemvArgs& a, const uint16_t* X, float* Y,
     constexpr int RPW = 64 / LPR;
     const int C = a.k >> 5;
     const size_t lds = (size_t)BT * 4 * C * 16 + (size_t)BT * C * 4;
-    static bool attr_set = false;  // per-process; the limit is the same on every gfx950 device
-    if (!attr_set) {
+    // The dynamic-LDS limit is a function attribute, set once per device.
+    std::atomic<int>& attr_set = PerDevice<&gemm_batched_kernel<LPR, BT>>::value[dev.device];
+    if (attr_set.load(std::memory_order_acquire) == 0) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_batched_kernel<LPR, BT>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dev.max_lds);
         if (e != hipSuccess) return e;
-        attr_set = true;
+        attr_set.store(1, std::memory_order_release);
     }
     const long passes = ((long)a.n + RPW - 1) / RPW;
     const int waves = 8;
@@ -512,8 +515,9 @@ static hipError_t launch_cols(const GemvArgs& a, const uint16_t* X, float* Y, in
     constexpr int kThreads = cols_threads<LPR, CPL>();
     const int C = a.k >> 5;
     const size_t lds = (size_t)BT * 4 * C * 16 + (size_t)BT * C * 4;
-    // Per process: the LDS limit and the register footprint are the same on every gfx950 device.
-    static int per_cu = 0;
+    // Once per device: the dynamic-LDS attribute, then the occupancy it allows.
+    std::atomic<int>& cached = PerDevice<&gemm_cols_kernel<LPR, CPL, BT>>::value[dev.device];
+    int per_cu = cached.load(std::memory_order_acquire);
     if (per_cu == 0) {
         const void* fn = reinterpret_cast<const void*>(&gemm_cols_kernel<LPR, CPL, BT>);
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dev.max_lds);
@@ -522,6 +526,7 @@ static hipError_t launch_cols(const GemvArgs& a, const uint16_t* X, float* Y, in
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb_cu, fn, kThreads, lds);
         if (e != hipSuccess) return e;
         per_cu = nb_cu > 0 ? nb_cu : 1;
+        cached.store(per_cu, std::memory_order_release);
     }
     const long passes = ((long)a.n + RPW - 1) / RPW;
     long grid = (long)dev.num_cu * per_cu;

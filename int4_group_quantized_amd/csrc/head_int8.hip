@@ -136,13 +136,15 @@ template <int CPL, bool RAGGED>
 static hipError_t launch_head(const int8_t* q, const uint16_t* scales, const uint16_t* x, float* y, int n, int k,
                               const DeviceInfo& dev, hipStream_t st) {
     const size_t lds = (size_t)k * 2;
-    static int per_cu = 0;  // per process: the register footprint is the same on every gfx950 device
+    std::atomic<int>& cached = PerDevice<&head_int8_kernel<CPL, RAGGED>>::value[dev.device];
+    int per_cu = cached.load(std::memory_order_relaxed);  // once per device
     if (per_cu == 0) {
         int nb = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &nb, reinterpret_cast<const void*>(&head_int8_kernel<CPL, RAGGED>), kHeadThreads, 8192 * 2);
         if (e != hipSuccess) return e;
         per_cu = nb > 0 ? nb : 1;
+        cached.store(per_cu, std::memory_order_relaxed);
     }
     long grid = (long)dev.num_cu * per_cu;
     const long need = ((long)n + (kHeadThreads / 64) - 1) / (kHeadThreads / 64);

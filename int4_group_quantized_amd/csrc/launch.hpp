@@ -7,7 +7,22 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace q4 {
+
+constexpr int kMaxDevices = 64;  // device ordinals the library serves (checked by the C ABI)
+
+// A launch property computed once per device and kernel instantiation
+// (occupancy, a function attribute): 0 until set.  Racing first calls
+// compute the same value; release/acquire order makes a set attribute
+// visible to any thread that reads the flag.
+template <auto Kernel>
+struct PerDevice {
+    static std::atomic<int> value[kMaxDevices];
+};
+template <auto Kernel>
+std::atomic<int> PerDevice<Kernel>::value[kMaxDevices];
 
 struct DeviceInfo {
     int device = -1;
