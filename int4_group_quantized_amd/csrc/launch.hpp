@@ -53,6 +53,8 @@ hipError_t launch_small_batch(const GemvArgs& a, const uint16_t* X, float* Y, in
                               const DeviceInfo& dev, hipStream_t st);
 hipError_t launch_prefill(const GemvArgs& a, const uint16_t* X, float* Y, int m,
                           const DeviceInfo& dev, hipStream_t st);
+hipError_t launch_prefill_split(const GemvArgs& a, const uint16_t* X, float* Y, int m,
+                                const DeviceInfo& dev, hipStream_t st);
 hipError_t launch_prefill_epilogue(const GemvArgs& a, const uint16_t* X, float* Y, int m,
                                    const DeviceInfo& dev, hipStream_t st);
 

@@ -1,7 +1,8 @@
 // Prompt-processing contraction on the gfx950 matrix cores:
 //   Y[m][n] = sum_k fp16(code*scale + min)[n][k] * X[m][k],  fp32 accumulate.
-// Two kernels: prefill_kernel for up to 64 tokens (below) and
-// prefill_wide_kernel for more (further down).
+// Three kernels: prefill_split_kernel (prefill_split.hip) for up to 48
+// tokens, prefill_kernel for 49 to 64 tokens (below) and prefill_wide_kernel
+// for more (further down).
 //
 // prefill_kernel work split: one workgroup of 8 waves per CU-sized slice of rows.  The N
 // rows are cut into gridDim.x contiguous ranges of at most 128 rows (the
@@ -33,23 +34,6 @@ namespace q4 {
 
 constexpr int kPrefillWaves = 8;
 constexpr int kPrefillRowsPerBlock = 16 * kPrefillWaves;
-
-// fp16 weights of one chunk (packed codes q, scale and minimum of its
-// group), 16 pairs in the permuted pair order.
-__device__ __forceinline__ void weights_fp16(const u4 q, uint16_t sb, uint16_t mb, const DequantConsts& kc,
-                                             uint32_t wv[16]) {
-    h2 codes[16];
-    dequant_dword(q.x, kc, codes + 0);
-    dequant_dword(q.y, kc, codes + 4);
-    dequant_dword(q.z, kc, codes + 8);
-    dequant_dword(q.w, kc, codes + 12);
-    const _Float16 sh = __builtin_bit_cast(_Float16, sb);
-    const _Float16 mh = __builtin_bit_cast(_Float16, mb);
-    const h2 s2 = {sh, sh};
-    const h2 m2 = {mh, mh};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) wv[i] = as_u32(__builtin_elementwise_fma(codes[i], s2, m2));
-}
 
 template <int TT>
 __global__ void __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -390,12 +374,11 @@ hipError_t launch_prefill(const GemvArgs& a, const uint16_t* X, float* Y, int m,
     if (m > 192) return launch_wide<4>(a, X, Y, m, dev, st);
     if (m > 128) return launch_wide<3>(a, X, Y, m, dev, st);
     if (m > 64) return launch_wide<2>(a, X, Y, m, dev, st);
-    // Up to 64 tokens: every wave dequantises its own 16 rows into registers.
-    const int tiles = (m + 15) / 16;
-    if (tiles <= 1) return launch_tt<1>(a, X, Y, m, dev, st);
-    if (tiles <= 2) return launch_tt<2>(a, X, Y, m, dev, st);
-    if (tiles <= 3) return launch_tt<3>(a, X, Y, m, dev, st);
-    return launch_tt<4>(a, X, Y, m, dev, st);
+    // 49 to 64 tokens: every wave dequantises its own 16 rows for four token tiles.
+    if (m > 48) return launch_tt<4>(a, X, Y, m, dev, st);
+    // Up to 48 tokens: the waves of a workgroup split K, activations in registers
+    // (prefill_split.hip).
+    return launch_prefill_split(a, X, Y, m, dev, st);
 }
 
 }  // namespace q4

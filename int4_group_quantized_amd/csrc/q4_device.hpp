@@ -155,6 +155,23 @@ __device__ __forceinline__ void dequant_dword(uint32_t q, const DequantConsts& k
     out[3] = __builtin_elementwise_fma(as_h2(d), sixteenth, neg64);
 }
 
+// fp16 weights of one chunk (packed codes q, scale and minimum of its
+// group), 16 pairs in the permuted pair order.
+__device__ __forceinline__ void weights_fp16(const u4 q, uint16_t sb, uint16_t mb, const DequantConsts& kc,
+                                             uint32_t wv[16]) {
+    h2 codes[16];
+    dequant_dword(q.x, kc, codes + 0);
+    dequant_dword(q.y, kc, codes + 4);
+    dequant_dword(q.z, kc, codes + 8);
+    dequant_dword(q.w, kc, codes + 12);
+    const _Float16 sh = __builtin_bit_cast(_Float16, sb);
+    const _Float16 mh = __builtin_bit_cast(_Float16, mb);
+    const h2 s2 = {sh, sh};
+    const h2 m2 = {mh, mh};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) wv[i] = as_u32(__builtin_elementwise_fma(codes[i], s2, m2));
+}
+
 // Rank of workgroup b among the workgroups of its XCD, laid out XCD by XCD
 // (the dispatcher deals workgroups to the 8 XCDs round-robin, block b on
 // XCD b % 8): consecutive ranks then share one L2.

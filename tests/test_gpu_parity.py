@@ -198,7 +198,12 @@ def test_non_default_stream(dev):
 @pytest.mark.parametrize("mtok,n,k", [(1, 64, 128), (2, 70, 384), (15, 100, 512), (16, 128, 3072), (17, 65, 3072),
                                       (34, 200, 3072), (64, 129, 256), (65, 130, 640), (100, 33, 8192),
                                       (112, 128, 1024), (129, 300, 1536), (193, 45, 384), (300, 64, 2048),
-                                      (5, 40, 32768)])
+                                      (5, 40, 32768),
+                                      # K split over the waves of a workgroup (up to 48 tokens): three
+                                      # rounds with padded groups, two tiles per workgroup, eight tiles
+                                      # per workgroup, waves with no group, and the first size above it
+                                      (48, 300, 8192), (20, 8000, 384), (48, 32768, 256), (33, 2500, 640),
+                                      (49, 70, 3072)])
 def test_prefill_parity_shapes(dev, mtok, n, k):
     w = synth.weights(n, k, seed=mtok * 1000 + n)
     X = synth.activations(mtok, k, seed=mtok + 17)
