@@ -1,8 +1,9 @@
 // Prompt-processing contraction on the gfx950 matrix cores:
 //   Y[m][n] = sum_k fp16(code*scale + min)[n][k] * X[m][k],  fp32 accumulate.
-// Three kernels: prefill_split_kernel (prefill_split.hip) for up to 48
-// tokens, prefill_kernel for 49 to 64 tokens (below) and prefill_wide_kernel
-// for more (further down).
+// Four kernels: prefill_split_kernel (prefill_split.hip) for up to 48
+// tokens, prefill_kernel for 49 to 64 tokens (below), prefill_wide_kernel
+// for 65 to 192 (further down) and prefill_pair_kernel (prefill_pair.hip)
+// above.
 //
 // prefill_kernel work split: one workgroup of 8 waves per CU-sized slice of rows.  The N
 // rows are cut into gridDim.x contiguous ranges of at most 128 rows (the
@@ -370,8 +371,10 @@ static hipError_t launch_tt(const GemvArgs& a, const uint16_t* X, float* Y, int 
 
 hipError_t launch_prefill(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
                           hipStream_t st) {
-    // More than 64 tokens: weights dequantised once per workgroup into LDS.
-    if (m > 192) return launch_wide<4>(a, X, Y, m, dev, st);
+    // More than 192 tokens: blocks of 128 tokens, the blocks of a row slice on
+    // one XCD (prefill_pair.hip).
+    if (m > 192) return launch_prefill_pair(a, X, Y, m, dev, st);
+    // 65 to 192 tokens: weights dequantised once per workgroup into LDS.
     if (m > 128) return launch_wide<3>(a, X, Y, m, dev, st);
     if (m > 64) return launch_wide<2>(a, X, Y, m, dev, st);
     // 49 to 64 tokens: every wave dequantises its own 16 rows for four token tiles.

@@ -203,7 +203,10 @@ def test_non_default_stream(dev):
                                       # rounds with padded groups, two tiles per workgroup, eight tiles
                                       # per workgroup, waves with no group, and the first size above it
                                       (48, 300, 8192), (20, 8000, 384), (48, 32768, 256), (33, 2500, 640),
-                                      (49, 70, 3072)])
+                                      (49, 70, 3072),
+                                      # blocks of 128 tokens paired per row slice (above 192 tokens):
+                                      # 16 row tiles per workgroup, three and four blocks, a partial block
+                                      (193, 32768, 256), (257, 4100, 256), (500, 700, 640), (200, 3000, 1024)])
 def test_prefill_parity_shapes(dev, mtok, n, k):
     w = synth.weights(n, k, seed=mtok * 1000 + n)
     X = synth.activations(mtok, k, seed=mtok + 17)
