@@ -196,6 +196,8 @@ static hipError_t launch_epi(const GemvArgs& a, const uint16_t* X, float* Y, int
 
 hipError_t launch_prefill_epilogue(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
                                    hipStream_t st) {
+    // Up to 48 tokens: the waves of a workgroup split K (prefill_split.hip).
+    if (m <= 48) return launch_prefill_split_epilogue(a, X, Y, m, dev, st);
     const int tiles = (m + 15) / 16;
     if (tiles <= 1) return launch_epi<1>(a, X, Y, m, dev, st);
     if (tiles <= 2) return launch_epi<2>(a, X, Y, m, dev, st);

@@ -1,7 +1,11 @@
 // Prompt processing for up to 48 tokens with the activations held in
 // registers (the dense M-token contraction of the rumik-oss-1 write-up,
-// "Step 8: a prefill that stays int4"; fp16 weights as in prefill.hip):
-//   Y[m][n] = sum_k fp16(code*scale + min)[n][k] * X[m][k],  fp32 accumulate.
+// "Step 8: a prefill that stays int4"), in both forms of the library:
+//   fp16 weights (as prefill.hip):
+//     Y[m][n] = sum_k fp16(code*scale + min)[n][k] * X[m][k],  fp32 accumulate;
+//   EPI, scale and minimum on the result (as prefill_epilogue.hip):
+//     Y[m][n] = sum_g scale[n][g] * C_g[m][n] + min[n][g] * S_g[m],
+//     C_g = sum over the group of code * x on the matrix cores, S_g = sum of x.
 //
 // Work split: one workgroup of NW waves per slice of at most 128 rows (the N
 // rows cut into gridDim.x contiguous ranges, as for the other prefill
@@ -24,9 +28,13 @@
 // tokens past the ends are clamped copies whose results are not stored.
 //
 // v_mfma_f32_16x16x32_f16 step s (0..3) contracts dword s of every lane's
-// chunk: B = the lane's 8 fp16 weights in the pair order of dequant_dword,
-// A = the same 8 columns of token r of a token tile, permuted alike.  Output
-// lane layout: lane l holds tokens 4*(l/16)+i of weight row l%16.
+// chunk: B = the lane's 8 fp16 weights (EPI: the 8 exact codes as fp16
+// denormals c * 2^-20) in the pair order of dequant_dword, A = the same 8
+// columns of token r of a token tile, permuted alike.  Output lane layout:
+// lane l holds tokens 4*(l/16)+i of weight row l%16.  In the EPI form each
+// group starts from a zero accumulator, and y += (scale * 2^20) * C_g and
+// y += min * S_g follow in fp32, with S_g of each output's token computed
+// once per round from the activation fragments and kept in LDS.
 #include "q4_device.hpp"
 #include "launch.hpp"
 
@@ -35,7 +43,7 @@ namespace q4 {
 constexpr int kSplitWaves = 8;
 constexpr int kSplitMaxTiles = 8;  // 16-row tiles per workgroup (128 rows)
 
-template <int TT, int GR, int NW>
+template <int TT, int GR, int NW, bool EPI>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 prefill_split_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
                      const uint16_t* __restrict__ mins, const uint16_t* __restrict__ X,
@@ -43,6 +51,7 @@ prefill_split_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restr
     extern __shared__ f4 lds_f4[];
     f4* part = lds_f4;                         // [2][NW][TT][64] partial sums per tile parity
     f4* tot = lds_f4 + 2 * NW * TT * 64;       // [kSplitMaxTiles][TT][64] totals of the slice
+    f4* gsum = tot + kSplitMaxTiles * TT * 64;  // EPI: [NW][GR][TT][64] per-token group sums
     constexpr int PER_ROUND = NW * GR;
 
     const int tid = threadIdx.x;
@@ -94,6 +103,32 @@ prefill_split_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restr
                 for (int s = 0; s < 4; ++s) xa[gi][s][t] = permute_window(xp[s]);
             }
         }
+        if constexpr (EPI) {
+            // S_g for the tokens of this lane's outputs (4q + i of each token
+            // tile): the lane's 32 columns of token r, then the other three
+            // k-slots of the token (lanes r + 16j), then fetched by token.
+            const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+            for (int gi = 0; gi < GR; ++gi)
+#pragma unroll
+                for (int t = 0; t < TT; ++t) {
+                    float v = 0.0f;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const u4 w = xa[gi][s][t];
+                        v = __builtin_amdgcn_fdot2(as_h2(w.x), ones, v, false);
+                        v = __builtin_amdgcn_fdot2(as_h2(w.y), ones, v, false);
+                        v = __builtin_amdgcn_fdot2(as_h2(w.z), ones, v, false);
+                        v = __builtin_amdgcn_fdot2(as_h2(w.w), ones, v, false);
+                    }
+                    v = v + lane_swap16(v);
+                    v = v + __shfl_xor(v, 32, 64);
+                    f4 sg;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sg[i] = __shfl(v, 4 * q + i, 64);
+                    gsum[((wave * GR + gi) * TT + t) * 64 + lane] = sg;
+                }
+        }
 
         auto tile = [&](int rt, int p) {
             const f4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -103,17 +138,47 @@ prefill_split_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restr
 #pragma unroll
             for (int gi = 0; gi < GR; ++gi) {
                 const uint32_t keep = (uint32_t)__builtin_amdgcn_readfirstlane(-(int)(gw + gi < G));
-                uint32_t wv[16];
-                weights_fp16(wq[p][gi], (uint16_t)(ws[p][gi] & keep), (uint16_t)(wm[p][gi] & keep), kc, wv);
-                load_w(p, gi, rt + 2);
+                if constexpr (EPI) {
+                    // Exact codes as fp16 denormals c * 2^-20 (each nibble moved
+                    // to mantissa bits 4..7), in the pair order of dequant_dword.
+                    const float sf = f16_bits_to_f32((uint16_t)(ws[p][gi] & keep)) * kInvUnit;
+                    const float mf = f16_bits_to_f32((uint16_t)(wm[p][gi] & keep));
+                    const u4 cw = wq[p][gi];
+                    load_w(p, gi, rt + 2);
+                    f4 cg[TT];
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const u4 bw = {wv[4 * s + 0], wv[4 * s + 1], wv[4 * s + 2], wv[4 * s + 3]};
-                    const h8 b = __builtin_bit_cast(h8, bw);
+                    for (int s = 0; s < 4; ++s) {
+                        const uint32_t d = s == 0 ? cw.x : s == 1 ? cw.y : s == 2 ? cw.z : cw.w;
+                        const u4 bw = {(d << 4) & 0x00F000F0u, d & 0x00F000F0u, (d >> 4) & 0x00F000F0u,
+                                       (d >> 8) & 0x00F000F0u};
+                        const h8 b = __builtin_bit_cast(h8, bw);
 #pragma unroll
-                    for (int t = 0; t < TT; ++t)
-                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[gi][s][t]), b,
-                                                                        acc[t], 0, 0, 0);
+                        for (int t = 0; t < TT; ++t)
+                            cg[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[gi][s][t]), b,
+                                                                           s == 0 ? zero : cg[t], 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int t = 0; t < TT; ++t) {
+                        const f4 sg = gsum[((wave * GR + gi) * TT + t) * 64 + lane];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            acc[t][i] = __builtin_fmaf(sf, cg[t][i], acc[t][i]);
+                            acc[t][i] = __builtin_fmaf(mf, sg[i], acc[t][i]);
+                        }
+                    }
+                } else {
+                    uint32_t wv[16];
+                    weights_fp16(wq[p][gi], (uint16_t)(ws[p][gi] & keep), (uint16_t)(wm[p][gi] & keep), kc, wv);
+                    load_w(p, gi, rt + 2);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const u4 bw = {wv[4 * s + 0], wv[4 * s + 1], wv[4 * s + 2], wv[4 * s + 3]};
+                        const h8 b = __builtin_bit_cast(h8, bw);
+#pragma unroll
+                        for (int t = 0; t < TT; ++t)
+                            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xa[gi][s][t]), b,
+                                                                            acc[t], 0, 0, 0);
+                    }
                 }
             }
 #pragma unroll
@@ -153,14 +218,15 @@ prefill_split_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restr
     }
 }
 
-template <int TT, int GR>
+template <int TT, int GR, bool EPI>
 static hipError_t launch_split(const GemvArgs& a, const uint16_t* X, float* Y, int m,
                                const DeviceInfo& dev, hipStream_t st) {
     constexpr int NW = kSplitWaves;
-    const size_t lds = ((size_t)2 * NW * TT + (size_t)kSplitMaxTiles * TT) * 64 * sizeof(f4);
-    std::atomic<int>& attr_set = PerDevice<&prefill_split_kernel<TT, GR, NW>>::value[dev.device];
+    const size_t lds = ((size_t)2 * NW * TT + (size_t)kSplitMaxTiles * TT + (EPI ? (size_t)NW * GR * TT : 0)) * 64 *
+                       sizeof(f4);
+    std::atomic<int>& attr_set = PerDevice<&prefill_split_kernel<TT, GR, NW, EPI>>::value[dev.device];
     if (attr_set.load(std::memory_order_acquire) == 0) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_split_kernel<TT, GR, NW>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_split_kernel<TT, GR, NW, EPI>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dev.max_lds);
         if (e != hipSuccess) return e;
         attr_set.store(1, std::memory_order_release);
@@ -172,12 +238,12 @@ static hipError_t launch_split(const GemvArgs& a, const uint16_t* X, float* Y, i
     if (grid < need) grid = need;
     const long tiles = ((long)a.n + 15) / 16;
     if (grid > tiles) grid = tiles;
-    hipLaunchKernelGGL((prefill_split_kernel<TT, GR, NW>), dim3((unsigned)grid), dim3(64 * NW), lds, st, a.packed,
-                       a.scales, a.mins, X, Y, a.n, a.k, m);
+    hipLaunchKernelGGL((prefill_split_kernel<TT, GR, NW, EPI>), dim3((unsigned)grid), dim3(64 * NW), lds, st,
+                       a.packed, a.scales, a.mins, X, Y, a.n, a.k, m);
     return hipGetLastError();
 }
 
-template <int TT>
+template <int TT, bool EPI>
 static hipError_t dispatch_split(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
                                  hipStream_t st) {
     // The fewest rounds at up to three groups per wave, then the fewest
@@ -186,20 +252,31 @@ static hipError_t dispatch_split(const GemvArgs& a, const uint16_t* X, float* Y,
     const int G = a.k >> 7;
     const int rounds = (G + kSplitWaves * kMaxGroupsPerWave - 1) / (kSplitWaves * kMaxGroupsPerWave);
     const int gr = (G + kSplitWaves * rounds - 1) / (kSplitWaves * rounds);
-    if (gr <= 1) return launch_split<TT, 1>(a, X, Y, m, dev, st);
-    if (gr <= 2) return launch_split<TT, 2>(a, X, Y, m, dev, st);
-    return launch_split<TT, 3>(a, X, Y, m, dev, st);
+    if (gr <= 1) return launch_split<TT, 1, EPI>(a, X, Y, m, dev, st);
+    if (gr <= 2) return launch_split<TT, 2, EPI>(a, X, Y, m, dev, st);
+    return launch_split<TT, 3, EPI>(a, X, Y, m, dev, st);
+}
+
+template <bool EPI>
+static hipError_t split_by_tokens(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
+                                  hipStream_t st) {
+    // At most three token tiles: the activation fragments of three groups of
+    // 48 tokens take 144 of the 256 registers a wave has at two waves per SIMD.
+    const int tiles = (m + 15) / 16;
+    if (tiles <= 1) return dispatch_split<1, EPI>(a, X, Y, m, dev, st);
+    if (tiles <= 2) return dispatch_split<2, EPI>(a, X, Y, m, dev, st);
+    if (tiles <= 3) return dispatch_split<3, EPI>(a, X, Y, m, dev, st);
+    return hipErrorInvalidValue;  // more than 48 tokens go to the other prefill kernels
 }
 
 hipError_t launch_prefill_split(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
                                 hipStream_t st) {
-    // At most three token tiles: the activation fragments of three groups of
-    // 48 tokens take 144 of the 256 registers a wave has at two waves per SIMD.
-    const int tiles = (m + 15) / 16;
-    if (tiles <= 1) return dispatch_split<1>(a, X, Y, m, dev, st);
-    if (tiles <= 2) return dispatch_split<2>(a, X, Y, m, dev, st);
-    if (tiles <= 3) return dispatch_split<3>(a, X, Y, m, dev, st);
-    return hipErrorInvalidValue;  // more than 48 tokens go to the other prefill kernels
+    return split_by_tokens<false>(a, X, Y, m, dev, st);
+}
+
+hipError_t launch_prefill_split_epilogue(const GemvArgs& a, const uint16_t* X, float* Y, int m,
+                                         const DeviceInfo& dev, hipStream_t st) {
+    return split_by_tokens<true>(a, X, Y, m, dev, st);
 }
 
 }  // namespace q4

@@ -42,7 +42,10 @@ def run(packed, s, m, X, dev):
 @pytest.mark.parametrize("mtok,n,k", [(1, 64, 128), (2, 70, 384), (15, 100, 512), (16, 128, 3072), (17, 65, 3072),
                                       (34, 300, 3072), (48, 129, 1152), (64, 129, 256), (65, 130, 640),
                                       (100, 257, 2048), (129, 300, 1536), (256, 96, 3072), (3, 33, 11008),
-                                      (5, 40, 32768)])
+                                      (5, 40, 32768),
+                                      # K split over the waves (up to 48 tokens): three rounds with padded
+                                      # groups, two tiles per workgroup, waves with no group
+                                      (48, 300, 8192), (20, 8000, 384), (33, 2500, 640)])
 def test_prefill_epilogue_parity(dev, mtok, n, k):
     w = synth.weights(n, k, seed=mtok * 1000 + n + 7)
     X = synth.activations(mtok, k, seed=mtok + 29)
