@@ -59,6 +59,8 @@ hipError_t launch_prefill_split_epilogue(const GemvArgs& a, const uint16_t* X, f
                                          const DeviceInfo& dev, hipStream_t st);
 hipError_t launch_prefill_pair(const GemvArgs& a, const uint16_t* X, float* Y, int m,
                                const DeviceInfo& dev, hipStream_t st);
+hipError_t launch_prefill_pair_epilogue(const GemvArgs& a, const uint16_t* X, float* Y, int m,
+                                        const DeviceInfo& dev, hipStream_t st);
 hipError_t launch_prefill_epilogue(const GemvArgs& a, const uint16_t* X, float* Y, int m,
                                    const DeviceInfo& dev, hipStream_t st);
 

@@ -11,6 +11,9 @@
 // rounded to fp16, so the result keeps the accuracy of the matrix-vector
 // kernels (every product code*x is exact; only fp32 sums round).
 //
+// This kernel serves 49 to 64 tokens; fewer go to prefill_split.hip and more
+// to prefill_pair.hip, in the same form.
+//
 // Work mapping (as the fp16-weight kernel for up to 64 tokens): one
 // workgroup of 8 waves per slice of at most 128 rows; wave w owns the 16-row
 // tile starting at row_lo + 16w; tokens are processed in blocks of 16*TT
@@ -198,11 +201,11 @@ hipError_t launch_prefill_epilogue(const GemvArgs& a, const uint16_t* X, float* 
                                    hipStream_t st) {
     // Up to 48 tokens: the waves of a workgroup split K (prefill_split.hip).
     if (m <= 48) return launch_prefill_split_epilogue(a, X, Y, m, dev, st);
-    const int tiles = (m + 15) / 16;
-    if (tiles <= 1) return launch_epi<1>(a, X, Y, m, dev, st);
-    if (tiles <= 2) return launch_epi<2>(a, X, Y, m, dev, st);
-    if (tiles <= 3) return launch_epi<3>(a, X, Y, m, dev, st);
-    return launch_epi<4>(a, X, Y, m, dev, st);  // blocks of 64 tokens beyond
+    // More than 64: blocks of 128 tokens per workgroup, the blocks of a row
+    // slice on one XCD (prefill_pair.hip).
+    if (m > 64) return launch_prefill_pair_epilogue(a, X, Y, m, dev, st);
+    // 49 to 64 tokens: four token tiles per wave (below).
+    return launch_epi<4>(a, X, Y, m, dev, st);
 }
 
 }  // namespace q4

@@ -1,7 +1,10 @@
-// Prompt processing for more than 192 tokens (the dense M-token contraction
-// of the rumik-oss-1 write-up, "Step 8: a prefill that stays int4"; fp16
-// weights as in prefill.hip):
-//   Y[m][n] = sum_k fp16(code*scale + min)[n][k] * X[m][k],  fp32 accumulate.
+// Prompt processing for many tokens (the dense M-token contraction of the
+// rumik-oss-1 write-up, "Step 8: a prefill that stays int4"), in both forms
+// of the library (above 192 tokens for fp16 weights, above 64 for EPI):
+//   fp16 weights (as prefill.hip):
+//     Y[m][n] = sum_k fp16(code*scale + min)[n][k] * X[m][k],  fp32 accumulate;
+//   EPI, scale and minimum on the result (as prefill_epilogue.hip):
+//     Y[m][n] = sum_g scale[n][g] * C_g[m][n] + min[n][g] * S_g[m].
 //
 // What bounds this shape is not the matrix cores but the activations: every
 // workgroup that covers all of K for its rows reads all of its tokens' X
@@ -12,8 +15,8 @@
 // of the slice's weights is served by the shared L2.
 //
 // Work split inside a workgroup of 8 waves (rows [row_lo, row_hi), at most
-// 16 row tiles of 16; tokens [tb*128, tb*128 + 128)):
-//  * wave w owns row tiles w and w + 8 (when they exist) for all 8 token
+// 16 row tiles of 16, 8 in the EPI form; tokens [tb*128, tb*128 + 128)):
+//  * wave w owns row tiles w and w + 8 (EPI: row tile w) for all 8 token
 //    tiles of the block: 16 accumulator tiles, 64 VGPRs;
 //  * it streams its tiles' packed codes, scales and mins four groups ahead
 //    and dequantises one dword (8 weights) per tile and k-step in registers,
@@ -26,6 +29,10 @@
 //  * v_mfma_f32_16x16x32_f16 step s (0..3) contracts dword s of every lane's
 //    chunk: B = the lane's 8 weights, A = the same 8 columns of token r of a
 //    token tile.  One LDS read of an A fragment serves the wave's row tiles.
+// EPI: B = the 8 exact codes as fp16 denormals c * 2^-20; each group's four
+// k-steps start from zero (two token tiles at a time) and are followed by
+// y += (scale * 2^20) * C_g + min * S_g in fp32, where S_g of every token is
+// summed by the wave that stages it and shared through LDS.
 // Groups past K are zero weights against clamped activations; rows and
 // tokens past the ends are clamped copies whose results are not stored.
 // Output lane layout: lane l holds tokens 4*(l/16)+i of weight row l%16.
@@ -35,20 +42,30 @@
 namespace q4 {
 
 constexpr int kPairWaves = 8;
-constexpr int kPairTokTiles = 8;              // token tiles per block (128 tokens)
-constexpr int kPairMaxRowTiles = 2 * kPairWaves;  // 256 rows per workgroup
-constexpr int kPairDW = 4;                    // weight groups in flight
-constexpr int kPairDX = 2;                    // activation groups in flight
+constexpr int kPairTokTiles = 8;  // token tiles per block (128 tokens)
+constexpr int kPairDW = 4;        // weight groups in flight
+constexpr int kPairDX = 2;        // activation groups in flight
 
+// Row tiles per wave: two in the fp16-weight form (256 rows per workgroup);
+// one in the epilogue form, whose running sums and per-group accumulators
+// (32 + 32 VGPRs per row tile) leave room for no second tile.
+template <bool EPI>
+constexpr int kPairRowTilesPerWave = EPI ? 1 : 2;
+
+// Two waves per SIMD in both forms.  The epilogue form needs 138 VGPRs; held
+// to 128 (two workgroups per CU) it spills in the group loop and measured
+// 101 against 89 us at M = 256.
+template <bool EPI>
 __global__ void __launch_bounds__(64 * kPairWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
                     const uint16_t* __restrict__ mins, const uint16_t* __restrict__ X,
                     float* __restrict__ Y, int n, int k, int m, int blocks) {
-    constexpr int TB = kPairTokTiles, DW = kPairDW, DX = kPairDX;
+    constexpr int TB = kPairTokTiles, DW = kPairDW, DX = kPairDX, RW = kPairRowTilesPerWave<EPI>;
     constexpr int U = 4;  // group loop unroll: a multiple of DW, DX and 2
     static_assert(U % DW == 0 && U % DX == 0 && U % 2 == 0, "ring depths");
     static_assert(TB == kPairWaves, "wave w stages token tile w");
     __shared__ u4 xs[2][TB][4][64];
+    __shared__ float xsum[2][TB][16];  // EPI: S_g of every token of the block
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -70,14 +87,14 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
     const int RT = (row_hi - row_lo + 15) >> 4;
     const int tok0 = tb * 16 * TB;
     if (RT == 0 || tok0 >= m) return;  // uniform: an empty slice or block
-    const bool two = wave + kPairWaves < RT;  // uniform: this wave has a second row tile
+    const bool two = RW == 2 && wave + kPairWaves < RT;  // uniform: this wave has a second row tile
 
     const size_t row_bytes = (size_t)(k >> 1);
-    const u4* cp[2];
-    const uint16_t* sp[2];
-    const uint16_t* mp[2];
+    const u4* cp[RW];
+    const uint16_t* sp[RW];
+    const uint16_t* mp[RW];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < RW; ++j) {
         int row = row_lo + 16 * (wave + kPairWaves * j) + r;
         row = row < row_hi ? row : row_hi - 1;
         cp[j] = reinterpret_cast<const u4*>(packed + (size_t)row * row_bytes) + q;
@@ -89,12 +106,12 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
     const u4* xp = reinterpret_cast<const u4*>(X + (size_t)xt * (size_t)k) + 4 * q;
     const DequantConsts kc = make_dequant_consts();
 
-    u4 wq[DW][2];
-    uint16_t ws[DW][2], wm[DW][2];
+    u4 wq[DW][RW];
+    uint16_t ws[DW][RW], wm[DW][RW];
     auto load_w = [&](int slot, int g) {
         const int gc = g < G ? g : G - 1;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < RW; ++j) {
             wq[slot][j] = __builtin_nontemporal_load(cp[j] + gc * 4);
             ws[slot][j] = sp[j][gc];
             wm[slot][j] = mp[j][gc];
@@ -107,8 +124,25 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
         for (int s = 0; s < 4; ++s) xq[slot][s] = xp[gc * 16 + s];
     };
     auto stage_x = [&](int slot, int buf) {
+        float v = 0.0f;
+        const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) xs[buf][wave][s][lane] = permute_window(xq[slot][s]);
+        for (int s = 0; s < 4; ++s) {
+            const u4 w = permute_window(xq[slot][s]);
+            xs[buf][wave][s][lane] = w;
+            if constexpr (EPI) {
+                v = __builtin_amdgcn_fdot2(as_h2(w.x), ones, v, false);
+                v = __builtin_amdgcn_fdot2(as_h2(w.y), ones, v, false);
+                v = __builtin_amdgcn_fdot2(as_h2(w.z), ones, v, false);
+                v = __builtin_amdgcn_fdot2(as_h2(w.w), ones, v, false);
+            }
+        }
+        if constexpr (EPI) {
+            // the token's four k-slots are lanes r, r + 16, r + 32, r + 48
+            v = v + lane_swap16(v);
+            v = v + __shfl_xor(v, 32, 64);
+            xsum[buf][wave][r] = v;  // the four lanes of the token write the same value
+        }
     };
 
 #pragma unroll
@@ -120,9 +154,9 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
     lds_barrier();
 
     const f4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    f4 acc[2][TB];
+    f4 acc[RW][TB];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < RW; ++j)
 #pragma unroll
         for (int t = 0; t < TB; ++t) acc[j][t] = zero;
 
@@ -131,35 +165,76 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
         for (int u = 0; u < U; ++u) {
             const int g = g0 + u;
             const int buf = u & 1;
-            const int ws_slot = u % DW;
+            const int slot = u % DW;
             const uint32_t keep = (uint32_t)__builtin_amdgcn_readfirstlane(-(int)(g < G));
-            const _Float16 s0 = __builtin_bit_cast(_Float16, (uint16_t)(ws[ws_slot][0] & keep));
-            const _Float16 m0 = __builtin_bit_cast(_Float16, (uint16_t)(wm[ws_slot][0] & keep));
-            const _Float16 s1 = __builtin_bit_cast(_Float16, (uint16_t)(ws[ws_slot][1] & keep));
-            const _Float16 m1 = __builtin_bit_cast(_Float16, (uint16_t)(wm[ws_slot][1] & keep));
-            const h2 sv[2] = {{s0, s0}, {s1, s1}};
-            const h2 mv[2] = {{m0, m0}, {m1, m1}};
-            const u4 cq[2] = {wq[ws_slot][0], wq[ws_slot][1]};
-            load_w(ws_slot, g + DW);
+            u4 cq[RW];
+            h2 sv[RW], mv[RW];
+            float sf[RW], mf[RW];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                h8 a[TB];
+            for (int j = 0; j < RW; ++j) {
+                cq[j] = wq[slot][j];
+                const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)(ws[slot][j] & keep));
+                const _Float16 mh = __builtin_bit_cast(_Float16, (uint16_t)(wm[slot][j] & keep));
+                sv[j] = (h2){sh, sh};
+                mv[j] = (h2){mh, mh};
+                sf[j] = (float)sh * kInvUnit;  // EPI: codes enter as c * 2^-20
+                mf[j] = (float)mh;
+            }
+            load_w(slot, g + DW);
+            if constexpr (EPI) {
+                // Exact codes as fp16 denormals c * 2^-20 (pair order of
+                // dequant_dword), then per pair of token tiles: the group's
+                // four k-steps from a zero accumulator and
+                // y += scale * C_g + min * S_g for the tokens 4q + i.
+                h8 b[4];
 #pragma unroll
-                for (int t = 0; t < TB; ++t) a[t] = __builtin_bit_cast(h8, xs[buf][t][s][lane]);
+                for (int s = 0; s < 4; ++s) {
+                    const uint32_t dw = s == 0 ? cq[0].x : s == 1 ? cq[0].y : s == 2 ? cq[0].z : cq[0].w;
+                    const u4 bw = {(dw << 4) & 0x00F000F0u, dw & 0x00F000F0u, (dw >> 4) & 0x00F000F0u,
+                                   (dw >> 8) & 0x00F000F0u};
+                    b[s] = __builtin_bit_cast(h8, bw);
+                }
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    if (j == 1 && !two) break;
-                    const uint32_t dw = s == 0 ? cq[j].x : s == 1 ? cq[j].y : s == 2 ? cq[j].z : cq[j].w;
-                    h2 c[4];
-                    dequant_dword(dw, kc, c);
-                    const u4 bw = {as_u32(__builtin_elementwise_fma(c[0], sv[j], mv[j])),
-                                   as_u32(__builtin_elementwise_fma(c[1], sv[j], mv[j])),
-                                   as_u32(__builtin_elementwise_fma(c[2], sv[j], mv[j])),
-                                   as_u32(__builtin_elementwise_fma(c[3], sv[j], mv[j]))};
-                    const h8 b = __builtin_bit_cast(h8, bw);
+                for (int t = 0; t < TB; t += 2) {
+                    f4 c0 = zero, c1 = zero;
 #pragma unroll
-                    for (int t = 0; t < TB; ++t)
-                        acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], b, acc[j][t], 0, 0, 0);
+                    for (int s = 0; s < 4; ++s) {
+                        const h8 a0 = __builtin_bit_cast(h8, xs[buf][t][s][lane]);
+                        const h8 a1 = __builtin_bit_cast(h8, xs[buf][t + 1][s][lane]);
+                        c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b[s], c0, 0, 0, 0);
+                        c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b[s], c1, 0, 0, 0);
+                    }
+                    const f4 s0 = *reinterpret_cast<const f4*>(&xsum[buf][t][4 * q]);
+                    const f4 s1 = *reinterpret_cast<const f4*>(&xsum[buf][t + 1][4 * q]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[0][t][i] = __builtin_fmaf(sf[0], c0[i], acc[0][t][i]);
+                        acc[0][t][i] = __builtin_fmaf(mf[0], s0[i], acc[0][t][i]);
+                        acc[0][t + 1][i] = __builtin_fmaf(sf[0], c1[i], acc[0][t + 1][i]);
+                        acc[0][t + 1][i] = __builtin_fmaf(mf[0], s1[i], acc[0][t + 1][i]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    h8 a[TB];
+#pragma unroll
+                    for (int t = 0; t < TB; ++t) a[t] = __builtin_bit_cast(h8, xs[buf][t][s][lane]);
+#pragma unroll
+                    for (int j = 0; j < RW; ++j) {
+                        if (j == 1 && !two) break;
+                        const uint32_t dw = s == 0 ? cq[j].x : s == 1 ? cq[j].y : s == 2 ? cq[j].z : cq[j].w;
+                        h2 c[4];
+                        dequant_dword(dw, kc, c);
+                        const u4 bw = {as_u32(__builtin_elementwise_fma(c[0], sv[j], mv[j])),
+                                       as_u32(__builtin_elementwise_fma(c[1], sv[j], mv[j])),
+                                       as_u32(__builtin_elementwise_fma(c[2], sv[j], mv[j])),
+                                       as_u32(__builtin_elementwise_fma(c[3], sv[j], mv[j]))};
+                        const h8 b = __builtin_bit_cast(h8, bw);
+#pragma unroll
+                        for (int t = 0; t < TB; ++t)
+                            acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], b, acc[j][t], 0, 0, 0);
+                    }
                 }
             }
             // the next group's activations: staged now, read after the barrier
@@ -170,7 +245,7 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
     }
 
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < RW; ++j) {
         const int row = row_lo + 16 * (wave + kPairWaves * j) + r;
         if (row < row_hi) {
 #pragma unroll
@@ -184,21 +259,34 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
     }
 }
 
-hipError_t launch_prefill_pair(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
-                               hipStream_t st) {
+template <bool EPI>
+static hipError_t launch_pair(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
+                              hipStream_t st) {
     // Token blocks of 128; row slices in multiples of 8 (one set per XCD),
-    // enough that every CU has a workgroup and no slice exceeds 256 rows.
+    // enough that every CU has a workgroup and no slice exceeds the rows of
+    // its waves' tiles.
+    const long rows_max = 16L * kPairWaves * kPairRowTilesPerWave<EPI>;
     const long blocks = ((long)m + 16 * kPairTokTiles - 1) / (16 * kPairTokTiles);
     const long cu = dev.num_cu > 0 ? dev.num_cu : 1;
     long slices = (cu + blocks - 1) / blocks;
-    const long need = ((long)a.n + 16 * kPairMaxRowTiles - 1) / (16 * kPairMaxRowTiles);
+    const long need = ((long)a.n + rows_max - 1) / rows_max;
     if (slices < need) slices = need;
     slices = ((slices + 7) / 8) * 8;
     const long grid = slices * blocks;
     if (grid > 0x7FFFFFFFL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(prefill_pair_kernel, dim3((unsigned)grid), dim3(64 * kPairWaves), 0, st, a.packed, a.scales,
-                       a.mins, X, Y, a.n, a.k, m, (int)blocks);
+    hipLaunchKernelGGL((prefill_pair_kernel<EPI>), dim3((unsigned)grid), dim3(64 * kPairWaves), 0, st, a.packed,
+                       a.scales, a.mins, X, Y, a.n, a.k, m, (int)blocks);
     return hipGetLastError();
+}
+
+hipError_t launch_prefill_pair(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
+                               hipStream_t st) {
+    return launch_pair<false>(a, X, Y, m, dev, st);
+}
+
+hipError_t launch_prefill_pair_epilogue(const GemvArgs& a, const uint16_t* X, float* Y, int m,
+                                        const DeviceInfo& dev, hipStream_t st) {
+    return launch_pair<true>(a, X, Y, m, dev, st);
 }
 
 }  // namespace q4

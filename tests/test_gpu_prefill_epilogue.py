@@ -45,7 +45,10 @@ def run(packed, s, m, X, dev):
                                       (5, 40, 32768),
                                       # K split over the waves (up to 48 tokens): three rounds with padded
                                       # groups, two tiles per workgroup, waves with no group
-                                      (48, 300, 8192), (20, 8000, 384), (33, 2500, 640)])
+                                      (48, 300, 8192), (20, 8000, 384), (33, 2500, 640),
+                                      # blocks of 128 tokens per workgroup (above 64 tokens): eight row
+                                      # tiles per workgroup, four blocks, a partial block
+                                      (193, 32768, 256), (500, 700, 640), (200, 3000, 1024)])
 def test_prefill_epilogue_parity(dev, mtok, n, k):
     w = synth.weights(n, k, seed=mtok * 1000 + n + 7)
     X = synth.activations(mtok, k, seed=mtok + 29)
