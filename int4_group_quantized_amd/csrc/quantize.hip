@@ -8,7 +8,9 @@
 // against the stored fp16 values, and code 0 everywhere when the stored scale
 // is 0.  Every step is one IEEE fp32 operation, correctly rounded (hipcc's
 // default division is the correctly rounded one, and contraction is off), so
-// the codes, scales and minimums are fully determined by the input.
+// the codes, scales and minimums are fully determined by the input.  The
+// per-value division is replaced by a reciprocal wherever that provably
+// gives the same code (code_from and near_half below).
 //
 // Mapping: the groups of all rows are one flat array (row n, group g is group
 // n*G + g; its 128 floats are contiguous, and so are its 64 packed bytes).
@@ -39,9 +41,23 @@ __device__ __forceinline__ void minmax32(float& lo, float& hi) {
     hi = fmaxf(hi, lane_swap16(hi));
 }
 
-__device__ __forceinline__ uint32_t code_of(float w, float mf, float sf) {
-    const float d = sf != 0.0f ? sf : 1.0f;
-    const float c = fminf(fmaxf(__builtin_rintf((w - mf) / d), 0.0f), 15.0f);
+// The code of one value: clamp(rne(RN(RN(w - min) / scale)), 0, 15), 0 when
+// the scale is 0.  The quotient is first formed with the hardware reciprocal,
+// q' = RN(RN(w - min) * rcp(scale)), within 2^-22 * |q| of the correctly
+// rounded q.  Only the half-integers 0.5 .. 14.5 separate different codes
+// (rne, then the clamp), and below 16 that error is under 2^-18; so when q'
+// lies more than 2^-16 from every half-integer, rne(q') = rne(q).  Lanes
+// where it does not are redone with the correctly rounded division (the
+// caller's `near` test), which keeps every code equal to the definition.
+__device__ __forceinline__ float quotient_fast(float w, float mf, float rs) { return (w - mf) * rs; }
+
+__device__ __forceinline__ int near_half(float q) {
+    const float e = __builtin_fabsf(q - __builtin_rintf(q));  // exact
+    return e > 0.5f - 1.52587890625e-05f;                     // 2^-16
+}
+
+__device__ __forceinline__ uint32_t code_from(float q, float sf) {
+    const float c = fminf(fmaxf(__builtin_rintf(q), 0.0f), 15.0f);
     return sf != 0.0f ? (uint32_t)c : 0u;
 }
 
@@ -66,8 +82,19 @@ quantize_kernel(const f4v* __restrict__ W, uint16_t* __restrict__ packed, uint16
         const _Float16 s16 = (_Float16)((hi - lo) / 15.0f);
         const _Float16 m16 = (_Float16)(lo + 0.0f);
         const float sf = (float)s16, mf = (float)m16;
-        const uint32_t c0 = code_of(v[u].x, mf, sf), c1 = code_of(v[u].y, mf, sf);
-        const uint32_t c2 = code_of(v[u].z, mf, sf), c3 = code_of(v[u].w, mf, sf);
+        const float rs = __builtin_amdgcn_rcpf(sf);
+        float q0 = quotient_fast(v[u].x, mf, rs), q1 = quotient_fast(v[u].y, mf, rs);
+        float q2 = quotient_fast(v[u].z, mf, rs), q3 = quotient_fast(v[u].w, mf, rs);
+        const int near = near_half(q0) | near_half(q1) | near_half(q2) | near_half(q3);
+        if (__ballot(near) != 0 && near) {  // rare: the correctly rounded quotients
+            const float d = sf != 0.0f ? sf : 1.0f;
+            q0 = (v[u].x - mf) / d;
+            q1 = (v[u].y - mf) / d;
+            q2 = (v[u].z - mf) / d;
+            q3 = (v[u].w - mf) / d;
+        }
+        const uint32_t c0 = code_from(q0, sf), c1 = code_from(q1, sf);
+        const uint32_t c2 = code_from(q2, sf), c3 = code_from(q3, sf);
         const long g = g0 + u;
         if (g < ngroups) {
             packed[g * 32 + lane] = (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));

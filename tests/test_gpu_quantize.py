@@ -79,6 +79,40 @@ def test_quantize_exact_round_trip(dev):
     assert np.array_equal(m, mins.view(np.uint16))
 
 
+def test_quantize_half_code_ties(dev):
+    """Quotients on and next to the half-integers that separate codes.
+
+    Dyadic rows (scale 2^-e, minimum a multiple of 2^-7): values m + (c + 1/2) s
+    are exact ties, resolved to the even code, and their fp32 neighbours fall
+    just either side.  Other rows take an arbitrary fp16 scale and minimum, so
+    m + (c + 1/2) s rounds to fp32 within an ulp or so of a tie.  Every code
+    must equal the oracle's, which divides with one correctly rounded fp32
+    division; the kernel reaches its quotient through a reciprocal and must
+    redo exactly these values."""
+    rng = np.random.Generator(np.random.PCG64(43))
+    n, k = 64, 1024
+    g = k // 128
+    c = rng.integers(0, 15, (n, k)).astype(np.float64) + 0.5  # half codes 0.5 .. 14.5
+    s = np.where(np.arange(n)[:, None] < n // 2,
+                 2.0 ** -rng.integers(3, 12, (n, g)),
+                 rng.uniform(0.001, 0.05, (n, g)).astype(np.float16).astype(np.float64))
+    m = np.where(np.arange(n)[:, None] < n // 2,
+                 -rng.integers(0, 257, (n, g)) / 128.0,
+                 -rng.uniform(0.0, 0.3, (n, g)).astype(np.float16).astype(np.float64))
+    s_full = np.repeat(s, 128, axis=1)
+    m_full = np.repeat(m, 128, axis=1)
+    W = (m_full + c * s_full).astype(np.float32)
+    nudge = rng.integers(-1, 2, (n, k))  # one fp32 ulp down, none, or up
+    W = np.where(nudge < 0, np.nextafter(W, np.float32(-np.inf)),
+                 np.where(nudge > 0, np.nextafter(W, np.float32(np.inf)), W)).astype(np.float32)
+    # codes 0 and 15 in every group, so that the range is 15 s from m
+    W[:, 0::128] = m_full[:, 0::128].astype(np.float32)
+    W[:, 1::128] = (m_full[:, 1::128] + 15.0 * s_full[:, 1::128]).astype(np.float32)
+    assert_same(gpu_quantize(W, dev), W)
+    codes, _, _ = oracle.quantize(W)
+    assert (codes % 2 == 0).sum() > 0 and (codes % 2 == 1).sum() > 0
+
+
 def test_quantize_full_size_sampled(dev):
     """The fused 25,088 x 3,072 projection in the benchmark's launch: sampled
     rows bit-exact against the oracle, every element within the reconstruction
