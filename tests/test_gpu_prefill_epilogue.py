@@ -48,7 +48,9 @@ def run(packed, s, m, X, dev):
                                       (48, 300, 8192), (20, 8000, 384), (33, 2500, 640),
                                       # blocks of 128 tokens per workgroup (above 64 tokens): eight row
                                       # tiles per workgroup, four blocks, a partial block
-                                      (193, 32768, 256), (500, 700, 640), (200, 3000, 1024)])
+                                      (193, 32768, 256), (500, 700, 640), (200, 3000, 1024),
+                                      # one and two rows: most workgroups have an empty slice
+                                      (7, 1, 128), (70, 2, 384)])
 def test_prefill_epilogue_parity(dev, mtok, n, k):
     w = synth.weights(n, k, seed=mtok * 1000 + n + 7)
     X = synth.activations(mtok, k, seed=mtok + 29)
