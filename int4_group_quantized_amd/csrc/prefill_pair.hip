@@ -46,24 +46,24 @@ constexpr int kPairTokTiles = 8;  // token tiles per block (128 tokens)
 constexpr int kPairDW = 4;        // weight groups in flight
 constexpr int kPairDX = 2;        // activation groups in flight
 
-// Row tiles per wave: two in the fp16-weight form (256 rows per workgroup);
-// one in the epilogue form, whose running sums and per-group accumulators
-// (32 + 32 VGPRs per row tile) leave room for no second tile.
-template <bool EPI>
-constexpr int kPairRowTilesPerWave = EPI ? 1 : 2;
-
-// Two waves per SIMD in both forms.  The epilogue form needs 138 VGPRs; held
-// to 128 (two workgroups per CU) it spills in the group loop and measured
-// 101 against 89 us at M = 256.
-template <bool EPI>
+// RW row tiles per wave (16 * 8 * RW rows per workgroup).  Two when a row
+// slice has several token blocks: one LDS read of an activation fragment then
+// serves two row tiles.  With a single block (up to 128 tokens) one, so that
+// every CU has a slice; a wave without a second tile in range still computes
+// it on clamped rows (results not stored), which costs nothing when another
+// wave of its SIMD has two (the busiest SIMD sets the time) and is
+// cheaper than a branch inside the group loop (measured: the epilogue form
+// then spills).
+template <bool EPI, int RW>
 __global__ void __launch_bounds__(64 * kPairWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
                     const uint16_t* __restrict__ mins, const uint16_t* __restrict__ X,
                     float* __restrict__ Y, int n, int k, int m, int blocks) {
-    constexpr int TB = kPairTokTiles, DW = kPairDW, DX = kPairDX, RW = kPairRowTilesPerWave<EPI>;
+    constexpr int TB = kPairTokTiles, DW = kPairDW, DX = kPairDX;
     constexpr int U = 4;  // group loop unroll: a multiple of DW, DX and 2
     static_assert(U % DW == 0 && U % DX == 0 && U % 2 == 0, "ring depths");
     static_assert(TB == kPairWaves, "wave w stages token tile w");
+    static_assert(RW == 1 || RW == 2, "row tiles per wave");
     __shared__ u4 xs[2][TB][4][64];
     __shared__ float xsum[2][TB][16];  // EPI: S_g of every token of the block
 
@@ -184,35 +184,44 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
             if constexpr (EPI) {
                 // Exact codes as fp16 denormals c * 2^-20 (pair order of
                 // dequant_dword), then per pair of token tiles: the group's
-                // four k-steps from a zero accumulator and
+                // four k-steps from a zero accumulator for each row tile and
                 // y += scale * C_g + min * S_g for the tokens 4q + i.
-                h8 b[4];
+                h8 b[RW][4];
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const uint32_t dw = s == 0 ? cq[0].x : s == 1 ? cq[0].y : s == 2 ? cq[0].z : cq[0].w;
-                    const u4 bw = {(dw << 4) & 0x00F000F0u, dw & 0x00F000F0u, (dw >> 4) & 0x00F000F0u,
-                                   (dw >> 8) & 0x00F000F0u};
-                    b[s] = __builtin_bit_cast(h8, bw);
-                }
+                for (int j = 0; j < RW; ++j)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const uint32_t dw = s == 0 ? cq[j].x : s == 1 ? cq[j].y : s == 2 ? cq[j].z : cq[j].w;
+                        const u4 bw = {(dw << 4) & 0x00F000F0u, dw & 0x00F000F0u, (dw >> 4) & 0x00F000F0u,
+                                       (dw >> 8) & 0x00F000F0u};
+                        b[j][s] = __builtin_bit_cast(h8, bw);
+                    }
 #pragma unroll
                 for (int t = 0; t < TB; t += 2) {
-                    f4 c0 = zero, c1 = zero;
+                    f4 c[RW][2];
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
                         const h8 a0 = __builtin_bit_cast(h8, xs[buf][t][s][lane]);
                         const h8 a1 = __builtin_bit_cast(h8, xs[buf][t + 1][s][lane]);
-                        c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b[s], c0, 0, 0, 0);
-                        c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b[s], c1, 0, 0, 0);
+#pragma unroll
+                        for (int j = 0; j < RW; ++j) {
+                            c[j][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b[j][s], s == 0 ? zero : c[j][0],
+                                                                             0, 0, 0);
+                            c[j][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b[j][s], s == 0 ? zero : c[j][1],
+                                                                             0, 0, 0);
+                        }
                     }
                     const f4 s0 = *reinterpret_cast<const f4*>(&xsum[buf][t][4 * q]);
                     const f4 s1 = *reinterpret_cast<const f4*>(&xsum[buf][t + 1][4 * q]);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc[0][t][i] = __builtin_fmaf(sf[0], c0[i], acc[0][t][i]);
-                        acc[0][t][i] = __builtin_fmaf(mf[0], s0[i], acc[0][t][i]);
-                        acc[0][t + 1][i] = __builtin_fmaf(sf[0], c1[i], acc[0][t + 1][i]);
-                        acc[0][t + 1][i] = __builtin_fmaf(mf[0], s1[i], acc[0][t + 1][i]);
-                    }
+                    for (int j = 0; j < RW; ++j)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            acc[j][t][i] = __builtin_fmaf(sf[j], c[j][0][i], acc[j][t][i]);
+                            acc[j][t][i] = __builtin_fmaf(mf[j], s0[i], acc[j][t][i]);
+                            acc[j][t + 1][i] = __builtin_fmaf(sf[j], c[j][1][i], acc[j][t + 1][i]);
+                            acc[j][t + 1][i] = __builtin_fmaf(mf[j], s1[i], acc[j][t + 1][i]);
+                        }
                 }
             } else {
 #pragma unroll
@@ -259,14 +268,12 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
     }
 }
 
-template <bool EPI>
-static hipError_t launch_pair(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
-                              hipStream_t st) {
-    // Token blocks of 128; row slices in multiples of 8 (one set per XCD),
-    // enough that every CU has a workgroup and no slice exceeds the rows of
-    // its waves' tiles.
-    const long rows_max = 16L * kPairWaves * kPairRowTilesPerWave<EPI>;
-    const long blocks = ((long)m + 16 * kPairTokTiles - 1) / (16 * kPairTokTiles);
+template <bool EPI, int RW>
+static hipError_t launch_pair(const GemvArgs& a, const uint16_t* X, float* Y, int m, long blocks,
+                              const DeviceInfo& dev, hipStream_t st) {
+    // Row slices in multiples of 8 (one set per XCD), enough that every CU
+    // has a workgroup and no slice exceeds the rows of its waves' tiles.
+    const long rows_max = 16L * kPairWaves * RW;
     const long cu = dev.num_cu > 0 ? dev.num_cu : 1;
     long slices = (cu + blocks - 1) / blocks;
     const long need = ((long)a.n + rows_max - 1) / rows_max;
@@ -274,19 +281,27 @@ static hipError_t launch_pair(const GemvArgs& a, const uint16_t* X, float* Y, in
     slices = ((slices + 7) / 8) * 8;
     const long grid = slices * blocks;
     if (grid > 0x7FFFFFFFL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prefill_pair_kernel<EPI>), dim3((unsigned)grid), dim3(64 * kPairWaves), 0, st, a.packed,
-                       a.scales, a.mins, X, Y, a.n, a.k, m, (int)blocks);
+    hipLaunchKernelGGL((prefill_pair_kernel<EPI, RW>), dim3((unsigned)grid), dim3(64 * kPairWaves), 0, st,
+                       a.packed, a.scales, a.mins, X, Y, a.n, a.k, m, (int)blocks);
     return hipGetLastError();
+}
+
+template <bool EPI>
+static hipError_t launch_pair_blocks(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
+                                     hipStream_t st) {
+    const long blocks = ((long)m + 16 * kPairTokTiles - 1) / (16 * kPairTokTiles);  // of 128 tokens
+    if (blocks == 1) return launch_pair<EPI, 1>(a, X, Y, m, blocks, dev, st);
+    return launch_pair<EPI, 2>(a, X, Y, m, blocks, dev, st);
 }
 
 hipError_t launch_prefill_pair(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
                                hipStream_t st) {
-    return launch_pair<false>(a, X, Y, m, dev, st);
+    return launch_pair_blocks<false>(a, X, Y, m, dev, st);
 }
 
 hipError_t launch_prefill_pair_epilogue(const GemvArgs& a, const uint16_t* X, float* Y, int m,
                                         const DeviceInfo& dev, hipStream_t st) {
-    return launch_pair<true>(a, X, Y, m, dev, st);
+    return launch_pair_blocks<true>(a, X, Y, m, dev, st);
 }
 
 }  // namespace q4
