@@ -158,7 +158,7 @@ prefill_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Wide prompt-processing kernel (more than 64 tokens).
+// Wide prompt-processing kernel (65 to 192 tokens).
 //
 // Workgroup of 8 waves on a slice of at most 128 rows (8 row tiles) and a
 // block of 64*TM tokens:
