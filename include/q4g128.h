@@ -89,8 +89,7 @@ Q4_API q4_status q4g128_pack(const uint8_t* codes, uint8_t* packed,
  * result: Y += scale * sum(code*x) + min * sum(x).  No weight is rounded to
  * fp16, so results carry only fp32 summation error (within 512 * 2^-24 *
  * sum_k |w*x| of the exact product).  Same arguments, limits, errors and
- * execution model as q4g128_gemm_prefill; any M >= 1 (blocks of 64 tokens
- * re-read the weights).
+ * execution model as q4g128_gemm_prefill; any M >= 1.
  */
 Q4_API q4_status q4g128_gemm_prefill_epilogue(const uint8_t* packed, const uint16_t* scales,
                                        const uint16_t* mins, const uint16_t* X, float* Y,
