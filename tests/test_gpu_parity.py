@@ -208,7 +208,9 @@ def test_non_default_stream(dev):
                                       # 16 row tiles per workgroup, three and four blocks, a partial block
                                       (193, 32768, 256), (257, 4100, 256), (500, 700, 640), (200, 3000, 1024),
                                       # one and three rows: most workgroups have an empty slice
-                                      (5, 1, 256), (300, 3, 384)])
+                                      (5, 1, 256), (300, 3, 384),
+                                      # the largest K with paired blocks
+                                      (200, 100, 32768)])
 def test_prefill_parity_shapes(dev, mtok, n, k):
     w = synth.weights(n, k, seed=mtok * 1000 + n)
     X = synth.activations(mtok, k, seed=mtok + 17)

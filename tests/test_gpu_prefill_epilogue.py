@@ -50,7 +50,9 @@ def run(packed, s, m, X, dev):
                                       # tiles per workgroup, four blocks, a partial block
                                       (193, 32768, 256), (500, 700, 640), (200, 3000, 1024),
                                       # one and two rows: most workgroups have an empty slice
-                                      (7, 1, 128), (70, 2, 384)])
+                                      (7, 1, 128), (70, 2, 384),
+                                      # large K with one and with two row tiles per wave
+                                      (100, 100, 16384), (150, 100, 32768)])
 def test_prefill_epilogue_parity(dev, mtok, n, k):
     w = synth.weights(n, k, seed=mtok * 1000 + n + 7)
     X = synth.activations(mtok, k, seed=mtok + 29)
