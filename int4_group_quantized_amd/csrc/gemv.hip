@@ -70,6 +70,30 @@ __device__ __forceinline__ void load_pass(PassLoad<CPL>& L, const uint8_t* __res
     }
 }
 
+// Activation staging: nw 16-byte windows, window w read by load(w) and written
+// by store(w, v), U windows per thread per batch.  A thread issues a batch's
+// loads before its first wait: a wait on the vector-memory counter also
+// covers the weight loads already in flight, and a wait per window would cost
+// one L2 round trip each (three at K = 11,008).  A slot past nw loads and
+// stores the thread's first window of the batch again (the same value to the
+// same place, at a distinct address per lane), so a batch has no branch for
+// the compiler to sink a load into.
+template <int U, typename Load, typename Store>
+__device__ __forceinline__ void stage_windows(int nw, Load load, Store store) {
+    const int step = (int)blockDim.x;
+    for (int w0 = (int)threadIdx.x; w0 < nw; w0 += U * step) {
+        u4 v[U];
+        int w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            w[u] = w0 + u * step < nw ? w0 + u * step : w0;
+            v[u] = load(w[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) store(w[u], v[u]);
+    }
+}
+
 template <int LPR, int CPL>
 __device__ __forceinline__ void compute_pass(const PassLoad<CPL>& L, const h2 (&xp)[CPL][16],
                                              const float (&xs)[CPL], float* __restrict__ y, int row,
@@ -118,8 +142,12 @@ gemv_reg_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__
 
     // Stage x: window w (8 halves) = quad (w & 3) of chunk (w >> 2).
     const u4* xv = reinterpret_cast<const u4*>(x);
-    for (int w = tid; w < (k >> 3); w += blockDim.x)
-        x_lds[(w & 3) * C + (w >> 2)] = permute_window(xv[w]);
+    // The longest row of this instantiation, K = 32 * LPR * CPL, has
+    // 4 * LPR * CPL windows: one batch covers them.
+    constexpr int kStage = (4 * LPR * CPL + kGemvThreads - 1) / kGemvThreads;
+    stage_windows<kStage>(
+        k >> 3, [&](int w) { return xv[w]; },
+        [&](int w, u4 v) { x_lds[(w & 3) * C + (w >> 2)] = permute_window(v); });
     __syncthreads();
 
     h2 xp[CPL][16];
