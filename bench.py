@@ -379,21 +379,33 @@ def main():
 
     forms = {}
     if not args.no_forms:
-        def gemv_form(name):
+        def gemv_form(name, batches=()):
             nn, kk, sd = synth.WORKLOADS[name]
             ww, xx = synth.gemv_case(nn, kk, sd)
             r = Rotation(torch, q4, ww, dev)
             yy = torch.empty(nn, dtype=torch.float32, device=dev)
             ms = time_checked(torch, stream, gemv_launcher(q4, r, f16(xx[0]), yy), yy, 1000, 20, GRAPH_LAUNCHES)
             b = algorithmic_bytes(nn, kk, 1)
+            out = {name + "_gemv_b1": {
+                "us_per_call": round(ms * 1e3, 3), "GB_per_s": round(b / (ms * 1e-3) / 1e9, 1),
+                "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "copies_rotated": -(-MALL_DEFEAT_BYTES // algorithmic_bytes(nn, kk, 0))}}
+            for nb in batches:
+                X = f16(synth.activations(nb, kk, sd + 1))
+                Y = torch.empty((nb, nn), dtype=torch.float32, device=dev)
+                msb = time_checked(torch, stream, batch_launcher(q4, r, X, Y, nb), Y, 1000, 20, GRAPH_LAUNCHES)
+                bb = algorithmic_bytes(nn, kk, nb)
+                out[f"{name}_small_batch_b{nb}"] = {
+                    "us_per_call": round(msb * 1e3, 3), "GB_per_s": round(bb / (msb * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(bb / (msb * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "speedup_vs_b_calls": round(nb * ms / msb, 3)}
             del r
-            return {"us_per_call": round(ms * 1e3, 3), "GB_per_s": round(b / (ms * 1e-3) / 1e9, 1),
-                    "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "copies_rotated": -(-MALL_DEFEAT_BYTES // algorithmic_bytes(nn, kk, 0))}
+            return out
 
-        forms["oproj_3072x3072_gemv_b1"] = gemv_form("oproj_3072x3072")
-        forms["down_3072x8192_gemv_b1"] = gemv_form("down_3072x8192")
+        forms.update(gemv_form("oproj_3072x3072"))
+        forms.update(gemv_form("down_3072x8192"))
         for name in ("pages_fused_25088x2048", "pages_oproj_2048x2048", "pages_down_2048x11008"):
-            forms[name + "_gemv_b1"] = gemv_form(name)
+            forms.update(gemv_form(name, batches=(16,)))
         for b in (2, 4, 8, 16):
             X = f16(synth.batch_activations(b))
             Y = torch.empty((b, n), dtype=torch.float32, device=dev)

@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libq4g128.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["api.cpp", "gemv.hip", "prefill.hip", "prefill_split.hip", "prefill_pair.hip", "prefill_epilogue.hip", "pack.hip",
+SOURCES = ["api.cpp", "gemv.hip", "gemv_seg.hip", "prefill.hip", "prefill_split.hip", "prefill_pair.hip", "prefill_epilogue.hip", "pack.hip",
            "quantize.hip", "head_int8.hip"]
 ARCH = "gfx950"
 

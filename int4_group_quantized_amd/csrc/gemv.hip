@@ -618,6 +618,17 @@ hipError_t launch_small_batch(const GemvArgs& a, const uint16_t* X, float* Y, in
     const int C = a.k >> 5;
     const bool ragged = C % lpr != 0;
     const int cap = max_cols_per_launch(a.k, dev);
+    // The slot-by-slot kernel (gemv_seg.hip) when the columns do not all fit
+    // in LDS (instead of one launch, and one weight read, per LDS-full), and
+    // from three columns on when its one-workgroup-per-CU grid covers every
+    // row in one round (at most two passes per wave): measured faster there
+    // for every shape tried but 3,072 x 8,192 at B = 3 and 4 (0.4 us).
+    const long passes = ((long)a.n * lpr + 63) / 64;
+    const bool one_round = passes <= 16L * dev.num_cu;
+    if (b > cap || (one_round && b >= 3)) {
+        hipError_t e = launch_small_batch_segmented(a, X, Y, b, dev, st);
+        if (e != hipErrorNotSupported) return e;
+    }
     for (int b0 = 0; b0 < b; b0 += cap) {
         const int nb = (b - b0) < cap ? (b - b0) : cap;
         const int bt = round_up_pow2_batch(nb);

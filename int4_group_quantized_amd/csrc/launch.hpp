@@ -51,6 +51,10 @@ hipError_t launch_head_int8(const int8_t* q, const uint16_t* scales, const uint1
 hipError_t launch_gemv(const GemvArgs& a, const DeviceInfo& dev, hipStream_t st);
 hipError_t launch_small_batch(const GemvArgs& a, const uint16_t* X, float* Y, int b,
                               const DeviceInfo& dev, hipStream_t st);
+// hipErrorNotSupported when the shape has no segmented form (LPR below 16, or
+// the two staging buffers exceed the LDS).
+hipError_t launch_small_batch_segmented(const GemvArgs& a, const uint16_t* X, float* Y, int b,
+                                        const DeviceInfo& dev, hipStream_t st);
 hipError_t launch_prefill(const GemvArgs& a, const uint16_t* X, float* Y, int m,
                           const DeviceInfo& dev, hipStream_t st);
 hipError_t launch_prefill_split(const GemvArgs& a, const uint16_t* X, float* Y, int m,

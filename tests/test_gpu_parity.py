@@ -141,8 +141,13 @@ def test_gemv_zero_and_scaling(dev):
 # batch: bit-identity with the batch-1 call, and parity
 # --------------------------------------------------------------------------
 
+# Above the batch that fits in LDS (8 columns at K = 8,192, 4 at 11,008, 2 at
+# 32,768) the rows are staged slot by slot; K = 5,120 / 7,168 and 5,632 take
+# that path with 32 and 16 lanes per row, and more than 2,048 passes (3,072,
+# 2,100 and 4,500 rows; 8,300 rows of 16 lanes) give each wave two of them.
 @pytest.mark.parametrize("n,k", [(25088, 3072), (3072, 8192), (257, 512), (100, 11008), (33, 384), (9, 32768),
-                                 (2048, 11008), (300, 2176), (64, 12160), (50, 12416)])
+                                 (2048, 11008), (300, 2176), (64, 12160), (50, 12416),
+                                 (130, 5120), (70, 5632), (33, 7168), (2100, 11008), (4500, 5120), (8300, 5632)])
 def test_small_batch_bit_identical_to_gemv(dev, n, k):
     w = synth.weights(n, k, seed=n + k)
     packed, s, m = upload(w, dev, q4)
@@ -164,6 +169,19 @@ def test_small_batch_parity_fused(dev, b):
     ref = oracle.gemm(packed_np, w.scales, w.mins, X)
     assert_rel(Y, ref, f"batch B={b}")
     assert_bound(Y, ref, oracle.term_magnitude(packed_np, w.scales, w.mins, X), 128, f"batch B={b}")
+
+
+@pytest.mark.parametrize("b", [5, 16])
+def test_small_batch_parity_pages_down(dev, b):
+    # 2,048 x 11,008 (ragged rows): more columns than fit in LDS
+    w = synth.weights(2048, 11008, seed=11)
+    X = synth.activations(b, 11008, seed=12)
+    packed_np = oracle.pack(w.codes)
+    packed, s, m = upload(w, dev, q4)
+    Y = cpu(q4.q4g128_gemm_small_batch(packed, s, m, to_dev_f16(X, dev)))
+    ref = oracle.gemm(packed_np, w.scales, w.mins, X)
+    assert_rel(Y, ref, f"pages' down B={b}")
+    assert_bound(Y, ref, oracle.term_magnitude(packed_np, w.scales, w.mins, X), 128, f"pages' down B={b}")
 
 
 def test_determinism_and_row_permutation(dev):
