@@ -3,9 +3,10 @@
 // Work mapping (depends on K only, never on the batch size, so that every
 // batched output column repeats the batch-1 arithmetic bit for bit):
 //   C   = K / 32 chunks per row (a chunk = 16 packed bytes = 32 codes);
-//   LPR = lanes per row: the largest of 64, 32, 16 dividing C; otherwise 64
-//         if C > 64 ("ragged": the last chunk column of a row is partial),
-//         else the largest of 8, 4 dividing C;
+//   LPR = lanes per row: 32 if C = 64 (K = 2,048), else the largest of 64,
+//         32, 16 dividing C; otherwise 64 if C > 64 ("ragged": the last
+//         chunk column of a row is partial), else the largest of 8, 4
+//         dividing C;
 //   CPL = ceil(C / LPR) chunks per lane; lane j of a row owns chunks
 //         j + t*LPR that are below C.  A ragged lane's missing chunk is
 //         either skipped or fed zero activations, which leaves its sum
@@ -431,6 +432,10 @@ gemm_batched_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
 
 int lanes_per_row(int k) {
     const int C = k >> 5;
+    // K = 2,048: one chunk per lane at 64 lanes would spend a full-wave
+    // butterfly per row (and per batch column) on 64 chunks; 32 lanes of two
+    // chunks measured faster at every batch size.
+    if (C == 64) return 32;
     if (C % 64 == 0) return 64;
     if (C % 32 == 0) return 32;
     if (C % 16 == 0) return 16;
@@ -474,7 +479,7 @@ static hipError_t dispatch_reg(int lpr, int cpl, bool ragged, const GemvArgs& a,
 #define Q4_REG_R(L, P) \
     if (ragged && lpr == L && cpl == P) return launch_reg<L, P, true>(a, dev, st);
     Q4_REG(64, 1) Q4_REG(64, 2) Q4_REG(64, 3) Q4_REG(64, 4)
-    Q4_REG(32, 1) Q4_REG(32, 3)
+    Q4_REG(32, 1) Q4_REG(32, 2) Q4_REG(32, 3)
     Q4_REG(16, 1) Q4_REG(16, 3)
     Q4_REG(8, 1) Q4_REG(8, 3)
     Q4_REG(4, 1) Q4_REG(4, 3)
@@ -578,7 +583,7 @@ static hipError_t dispatch_cols(int lpr, int cpl, int bt, const GemvArgs& a, con
             case 16: return launch_cols<L, P, 16>(a, X, Y, nb, dev, st);       \
         }                                                                      \
     }
-    Q4_COLS(32, 3) Q4_COLS(64, 4) Q4_COLS(16, 1) Q4_COLS(64, 1) Q4_COLS(64, 2)
+    Q4_COLS(32, 3) Q4_COLS(32, 2) Q4_COLS(64, 4) Q4_COLS(16, 1) Q4_COLS(64, 1) Q4_COLS(64, 2)
 #undef Q4_COLS
     return hipErrorNotSupported;
 }

@@ -24,25 +24,28 @@
 
 namespace q4 {
 
+// Waves per workgroup: 8, or 4 for matrices of at most 4 passes per CU.
 constexpr int kSegWaves = 8;
-constexpr int kSegThreads = 64 * kSegWaves;
 
 // Staging unit: chunk jj of slot t for column b = 64 bytes of X (4 windows).
 // One thread permutes the unit's windows and sums its 32 activations in the
 // fixed chunk_xsum order.
-template <int LPR, int BT>
+template <int LPR, int BT, int NW>
 struct SegStage {
+    static constexpr int kThreads = 64 * NW;
     static constexpr int kUnits = BT * LPR;
-    static constexpr int kPerThread = (kUnits + kSegThreads - 1) / kSegThreads;
+    static constexpr int kPerThread = (kUnits + kThreads - 1) / kThreads;
     u4 v[kPerThread][4];
 };
 
-template <int LPR, int BT>
-__device__ __forceinline__ void seg_issue(SegStage<LPR, BT>& S, const uint16_t* __restrict__ X, int k, int nb, int t) {
+template <int LPR, int BT, int NW>
+__device__ __forceinline__ void seg_issue(SegStage<LPR, BT, NW>& S, const uint16_t* __restrict__ X, int k, int nb,
+                                          int t) {
+    using St = SegStage<LPR, BT, NW>;
     const int C = k >> 5;
 #pragma unroll
-    for (int i = 0; i < SegStage<LPR, BT>::kPerThread; ++i) {
-        const int u = (int)threadIdx.x + i * kSegThreads;
+    for (int i = 0; i < St::kPerThread; ++i) {
+        const int u = (int)threadIdx.x + i * St::kThreads;
         const int b = u / LPR;
         const int c = t * LPR + (u % LPR);
         // Clamped so that every load is in range; invalid units are zeroed
@@ -50,7 +53,7 @@ __device__ __forceinline__ void seg_issue(SegStage<LPR, BT>& S, const uint16_t* 
         const int bc = b < nb ? b : nb - 1;
         const int cc = c < C ? c : C - 1;
         const u4* src = reinterpret_cast<const u4*>(X + (size_t)bc * (size_t)k) + (size_t)cc * 4;
-        if (u < SegStage<LPR, BT>::kUnits) {
+        if (u < St::kUnits) {
 #pragma unroll
             for (int d = 0; d < 4; ++d) S.v[i][d] = src[d];
         }
@@ -58,14 +61,15 @@ __device__ __forceinline__ void seg_issue(SegStage<LPR, BT>& S, const uint16_t* 
 }
 
 // LDS buffer: windows [BT][4][LPR] (16 bytes each), then sums [BT][LPR].
-template <int LPR, int BT>
-__device__ __forceinline__ void seg_store(const SegStage<LPR, BT>& S, u4* __restrict__ xq, float* __restrict__ xsm,
-                                          int k, int nb, int t) {
+template <int LPR, int BT, int NW>
+__device__ __forceinline__ void seg_store(const SegStage<LPR, BT, NW>& S, u4* __restrict__ xq,
+                                          float* __restrict__ xsm, int k, int nb, int t) {
+    using St = SegStage<LPR, BT, NW>;
     const int C = k >> 5;
 #pragma unroll
-    for (int i = 0; i < SegStage<LPR, BT>::kPerThread; ++i) {
-        const int u = (int)threadIdx.x + i * kSegThreads;
-        if (u < SegStage<LPR, BT>::kUnits) {
+    for (int i = 0; i < St::kPerThread; ++i) {
+        const int u = (int)threadIdx.x + i * St::kThreads;
+        if (u < St::kUnits) {
             const int b = u / LPR;
             const int jj = u % LPR;
             const uint32_t keep = (b < nb && t * LPR + jj < C) ? 0xFFFFFFFFu : 0u;
@@ -106,8 +110,8 @@ __device__ __forceinline__ void seg_weights(SegWeights& W, const uint8_t* __rest
     W.m = mins[g];
 }
 
-template <int LPR, int BT, int R>
-__global__ void __launch_bounds__(kSegThreads)
+template <int LPR, int BT, int R, int NW>
+__global__ void __launch_bounds__(64 * NW)
 gemm_seg_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
                 const uint16_t* __restrict__ mins, const uint16_t* __restrict__ X, float* __restrict__ Y,
                 int n, int k, int nb) {
@@ -122,16 +126,16 @@ gemm_seg_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__
     int row[R], rowc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        row[r] = (((int)blockIdx.x * kSegWaves + wave) * R + r) * RPW + lane / LPR;
+        row[r] = (((int)blockIdx.x * NW + wave) * R + r) * RPW + lane / LPR;
         rowc[r] = row[r] < n ? row[r] : n - 1;
     }
 
     SegWeights W[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) seg_weights(W[r], packed, scales, mins, rowc[r], k, j);
-    SegStage<LPR, BT> S;
-    seg_issue<LPR, BT>(S, X, k, nb, 0);
-    seg_store<LPR, BT>(S, lds, reinterpret_cast<float*>(lds + BT * 4 * LPR), k, nb, 0);
+    SegStage<LPR, BT, NW> S;
+    seg_issue<LPR, BT, NW>(S, X, k, nb, 0);
+    seg_store<LPR, BT, NW>(S, lds, reinterpret_cast<float*>(lds + BT * 4 * LPR), k, nb, 0);
     lds_barrier();
 
     float y[R][BT];
@@ -148,7 +152,7 @@ gemm_seg_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__
         if (more) {
 #pragma unroll
             for (int r = 0; r < R; ++r) seg_weights(Wn[r], packed, scales, mins, rowc[r], k, (t + 1) * LPR + j);
-            seg_issue<LPR, BT>(S, X, k, nb, t + 1);
+            seg_issue<LPR, BT, NW>(S, X, k, nb, t + 1);
         }
         h2 codes[R][16];
 #pragma unroll
@@ -185,7 +189,7 @@ gemm_seg_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__
         }
         if (more) {
             u4* nq = lds + ((t + 1) & 1) * kBufU4;
-            seg_store<LPR, BT>(S, nq, reinterpret_cast<float*>(nq + BT * 4 * LPR), k, nb, t + 1);
+            seg_store<LPR, BT, NW>(S, nq, reinterpret_cast<float*>(nq + BT * 4 * LPR), k, nb, t + 1);
 #pragma unroll
             for (int r = 0; r < R; ++r) W[r] = Wn[r];
         }
@@ -201,36 +205,38 @@ gemm_seg_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__
         }
 }
 
-template <int LPR, int BT, int R>
+template <int LPR, int BT, int R, int NW>
 static hipError_t launch_seg(const GemvArgs& a, const uint16_t* X, float* Y, int nb, const DeviceInfo& dev,
                              hipStream_t st) {
     constexpr int RPW = 64 / LPR;
     const size_t lds = 2 * ((size_t)BT * 4 * LPR * 16 + (size_t)BT * LPR * 4);
     if (lds > dev.max_lds) return hipErrorNotSupported;
-    std::atomic<int>& attr_set = PerDevice<&gemm_seg_kernel<LPR, BT, R>>::value[dev.device];
+    std::atomic<int>& attr_set = PerDevice<&gemm_seg_kernel<LPR, BT, R, NW>>::value[dev.device];
     if (attr_set.load(std::memory_order_acquire) == 0) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_seg_kernel<LPR, BT, R>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_seg_kernel<LPR, BT, R, NW>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dev.max_lds);
         if (e != hipSuccess) return e;
         attr_set.store(1, std::memory_order_release);
     }
     const long passes = ((long)a.n + RPW - 1) / RPW;
-    const long per_block = (long)kSegWaves * R;
+    const long per_block = (long)NW * R;
     const long grid = (passes + per_block - 1) / per_block;
-    hipLaunchKernelGGL((gemm_seg_kernel<LPR, BT, R>), dim3((unsigned)grid), dim3(kSegThreads), lds, st, a.packed,
+    hipLaunchKernelGGL((gemm_seg_kernel<LPR, BT, R, NW>), dim3((unsigned)grid), dim3(64 * NW), lds, st, a.packed,
                        a.scales, a.mins, X, Y, a.n, a.k, nb);
     return hipGetLastError();
 }
 
 // Two passes per wave once one per wave would need more workgroups than CUs
-// (the staging buffers allow one workgroup per CU at 16 columns).
+// (the staging buffers allow one workgroup per CU at 16 columns); four waves
+// per workgroup when that still needs no more workgroups than CUs.
 template <int LPR, int BT>
 static hipError_t launch_seg_rows(const GemvArgs& a, const uint16_t* X, float* Y, int nb, const DeviceInfo& dev,
                                   hipStream_t st) {
     constexpr int RPW = 64 / LPR;
     const long passes = ((long)a.n + RPW - 1) / RPW;
-    if (passes > (long)kSegWaves * dev.num_cu) return launch_seg<LPR, BT, 2>(a, X, Y, nb, dev, st);
-    return launch_seg<LPR, BT, 1>(a, X, Y, nb, dev, st);
+    if (passes > (long)kSegWaves * dev.num_cu) return launch_seg<LPR, BT, 2, kSegWaves>(a, X, Y, nb, dev, st);
+    if (passes <= (long)(kSegWaves / 2) * dev.num_cu) return launch_seg<LPR, BT, 1, kSegWaves / 2>(a, X, Y, nb, dev, st);
+    return launch_seg<LPR, BT, 1, kSegWaves>(a, X, Y, nb, dev, st);
 }
 
 template <int LPR>
