@@ -48,14 +48,17 @@ __device__ __forceinline__ void seg_issue(SegStage<LPR, BT, NW>& S, const uint16
         const int u = (int)threadIdx.x + i * St::kThreads;
         const int b = u / LPR;
         const int c = t * LPR + (u % LPR);
-        // Clamped so that every load is in range; invalid units are zeroed
-        // when stored.
-        const int bc = b < nb ? b : nb - 1;
+        // Chunks past C load the last chunk (in range) and are zeroed when
+        // stored; columns past nb (whole waves at 64 lanes per row) load
+        // nothing.
         const int cc = c < C ? c : C - 1;
-        const u4* src = reinterpret_cast<const u4*>(X + (size_t)bc * (size_t)k) + (size_t)cc * 4;
-        if (u < St::kUnits) {
+        if (u < St::kUnits && b < nb) {
+            const u4* src = reinterpret_cast<const u4*>(X + (size_t)b * (size_t)k) + (size_t)cc * 4;
 #pragma unroll
             for (int d = 0; d < 4; ++d) S.v[i][d] = src[d];
+        } else {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) S.v[i][d] = u4{0u, 0u, 0u, 0u};
         }
     }
 }
@@ -246,6 +249,7 @@ static hipError_t dispatch_seg_bt(int bt, const GemvArgs& a, const uint16_t* X, 
         case 2: return launch_seg_rows<LPR, 2>(a, X, Y, nb, dev, st);
         case 4: return launch_seg_rows<LPR, 4>(a, X, Y, nb, dev, st);
         case 8: return launch_seg_rows<LPR, 8>(a, X, Y, nb, dev, st);
+        case 12: return launch_seg_rows<LPR, 12>(a, X, Y, nb, dev, st);
         case 16: return launch_seg_rows<LPR, 16>(a, X, Y, nb, dev, st);
     }
     return hipErrorNotSupported;
@@ -253,8 +257,10 @@ static hipError_t dispatch_seg_bt(int bt, const GemvArgs& a, const uint16_t* X, 
 
 hipError_t launch_small_batch_segmented(const GemvArgs& a, const uint16_t* X, float* Y, int b,
                                         const DeviceInfo& dev, hipStream_t st) {
+    // Column slots: 2, 4, 8, 12 or 16 (columns past b are zero and not stored).
     int bt = 2;
     while (bt < b) bt <<= 1;
+    if (b > 8 && b <= 12) bt = 12;
     switch (lanes_per_row(a.k)) {
         case 64: return dispatch_seg_bt<64>(bt, a, X, Y, b, dev, st);
         case 32: return dispatch_seg_bt<32>(bt, a, X, Y, b, dev, st);
