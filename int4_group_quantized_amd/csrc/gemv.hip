@@ -580,6 +580,7 @@ static hipError_t dispatch_cols(int lpr, int cpl, int bt, const GemvArgs& a, con
             case 2: return launch_cols<L, P, 2>(a, X, Y, nb, dev, st);         \
             case 4: return launch_cols<L, P, 4>(a, X, Y, nb, dev, st);         \
             case 8: return launch_cols<L, P, 8>(a, X, Y, nb, dev, st);         \
+            case 12: return launch_cols<L, P, 12>(a, X, Y, nb, dev, st);       \
             case 16: return launch_cols<L, P, 16>(a, X, Y, nb, dev, st);       \
         }                                                                      \
     }
@@ -637,10 +638,12 @@ hipError_t launch_small_batch(const GemvArgs& a, const uint16_t* X, float* Y, in
     for (int b0 = 0; b0 < b; b0 += cap) {
         const int nb = (b - b0) < cap ? (b - b0) : cap;
         const int bt = round_up_pow2_batch(nb);
+        // The column kernel also has a 12-column form (9 to 12 columns).
+        const int bt_cols = nb > 8 && nb <= 12 && 12 <= cap ? 12 : bt;
         const uint16_t* Xc = X + (size_t)b0 * (size_t)a.k;
         float* Yc = Y + (size_t)b0 * (size_t)a.n;
         // The columns kernel has no ragged rows; those go to the batched kernel.
-        hipError_t e = ragged ? hipErrorNotSupported : dispatch_cols(lpr, C / lpr, bt, a, Xc, Yc, nb, dev, st);
+        hipError_t e = ragged ? hipErrorNotSupported : dispatch_cols(lpr, C / lpr, bt_cols, a, Xc, Yc, nb, dev, st);
         if (e == hipErrorNotSupported) e = dispatch_batched(lpr, bt, a, Xc, Yc, nb, dev, st);
         if (e != hipSuccess) return e;
     }
