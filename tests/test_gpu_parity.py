@@ -147,7 +147,8 @@ def test_gemv_zero_and_scaling(dev):
 # 2,100 and 4,500 rows; 8,300 rows of 16 lanes) give each wave two of them.
 @pytest.mark.parametrize("n,k", [(25088, 3072), (3072, 8192), (257, 512), (100, 11008), (33, 384), (9, 32768),
                                  (2048, 11008), (300, 2176), (64, 12160), (50, 12416),
-                                 (130, 5120), (70, 5632), (33, 7168), (2100, 11008), (4500, 5120), (8300, 5632)])
+                                 (130, 5120), (70, 5632), (33, 7168), (2100, 11008), (4500, 5120), (8300, 5632),
+                                 (1, 11008), (5, 2048), (3, 1024)])
 def test_small_batch_bit_identical_to_gemv(dev, n, k):
     w = synth.weights(n, k, seed=n + k)
     packed, s, m = upload(w, dev, q4)
