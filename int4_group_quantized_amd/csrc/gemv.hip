@@ -626,12 +626,13 @@ hipError_t launch_small_batch(const GemvArgs& a, const uint16_t* X, float* Y, in
     const int cap = max_cols_per_launch(a.k, dev);
     // The slot-by-slot kernel (gemv_seg.hip) when the columns do not all fit
     // in LDS (instead of one launch, and one weight read, per LDS-full), and
-    // from three columns on when its one-workgroup-per-CU grid covers every
-    // row in one round (at most two passes per wave): measured faster there
-    // for every shape tried but 3,072 x 8,192 at B = 3 and 4 (0.4 us).
+    // whenever its one-workgroup-per-CU grid covers every row in one round
+    // (at most two passes per wave): measured faster there for every shape
+    // tried but 3,072 x 8,192 at B = 2 (0.2 us).  Taller matrices keep the
+    // column kernel (25,088 x 3,072 at B = 16: 39 against 55 us).
     const long passes = ((long)a.n * lpr + 63) / 64;
     const bool one_round = passes <= 16L * dev.num_cu;
-    if (b > cap || (one_round && b >= 3)) {
+    if (b > cap || one_round) {
         hipError_t e = launch_small_batch_segmented(a, X, Y, b, dev, st);
         if (e != hipErrorNotSupported) return e;
     }

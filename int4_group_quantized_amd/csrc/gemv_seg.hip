@@ -1,7 +1,7 @@
 // Small-batch matmat, slot by slot: for rows too long for all B activation
 // columns to sit in LDS at once (16 columns of K = 11,008 would need 374 KB),
-// and from three columns on for matrices whose rows this grid covers in one
-// round (at most 4,096 passes on 256 CUs).
+// and for matrices whose rows this grid covers in one round (at most
+// 4,096 passes on 256 CUs).
 //
 // The work mapping is the batch-1 one (lanes per row LPR, lane j of a row
 // owns chunks j + t*LPR), walked one chunk slot t at a time: slot t covers
