@@ -31,8 +31,11 @@
 //    token tile.  One LDS read of an A fragment serves the wave's row tiles.
 // EPI: B = the 8 exact codes as fp16 denormals c * 2^-20; each group's four
 // k-steps start from zero (two token tiles at a time) and are followed by
-// y += (scale * 2^20) * C_g + min * S_g in fp32, where S_g of every token is
-// summed by the wave that stages it and shared through LDS.
+// y += (scale * 2^20) * C_g in fp32.  The minimum term, sum over g of
+// min_g * S_g, is a product of rank G: every four groups it goes to the matrix
+// cores as one v_mfma_f32_16x16x4_f32 per tile (A = the tokens' group sums
+// S_g, summed by the wave that stages the token and kept in an LDS ring of
+// eight groups; B = the rows' minimums), accumulated into the same tile.
 // Groups past K are zero weights against clamped activations; rows and
 // tokens past the ends are clamped copies whose results are not stored.
 // Output lane layout: lane l holds tokens 4*(l/16)+i of weight row l%16.
@@ -65,7 +68,7 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
     static_assert(TB == kPairWaves, "wave w stages token tile w");
     static_assert(RW == 1 || RW == 2, "row tiles per wave");
     __shared__ u4 xs[2][TB][4][64];
-    __shared__ float xsum[2][TB][16];  // EPI: S_g of every token of the block
+    __shared__ float xsum[8][TB][16];  // EPI: S_g of every token of the block, groups g mod 8
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -123,7 +126,7 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
 #pragma unroll
         for (int s = 0; s < 4; ++s) xq[slot][s] = xp[gc * 16 + s];
     };
-    auto stage_x = [&](int slot, int buf) {
+    auto stage_x = [&](int slot, int buf, int sg) {
         float v = 0.0f;
         const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
@@ -141,7 +144,7 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
             // the token's four k-slots are lanes r, r + 16, r + 32, r + 48
             v = v + lane_swap16(v);
             v = v + __shfl_xor(v, 32, 64);
-            xsum[buf][wave][r] = v;  // the four lanes of the token write the same value
+            xsum[sg][wave][r] = v;  // the four lanes of the token write the same value
         }
     };
 
@@ -149,7 +152,7 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
     for (int d = 0; d < DW; ++d) load_w(d, d);
 #pragma unroll
     for (int d = 0; d < DX; ++d) load_x(d, d);
-    stage_x(0, 0);
+    stage_x(0, 0, 0);
     load_x(0, DX);
     lds_barrier();
 
@@ -161,6 +164,16 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
         for (int t = 0; t < TB; ++t) acc[j][t] = zero;
 
     for (int g0 = 0; g0 < Gp; g0 += U) {
+        // EPI: this window's minimums, min[row][g0 + q] for lane (r, q) and
+        // each row tile (zero past G), requested four groups before use.
+        float mwin[RW];
+        if constexpr (EPI) {
+            const int gq = g0 + q;
+            const uint32_t live = (uint32_t)(-(int)(gq < G));
+#pragma unroll
+            for (int j = 0; j < RW; ++j)
+                mwin[j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(mp[j][gq < G ? gq : G - 1] & live));
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int g = g0 + u;
@@ -169,7 +182,7 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
             const uint32_t keep = (uint32_t)__builtin_amdgcn_readfirstlane(-(int)(g < G));
             u4 cq[RW];
             h2 sv[RW], mv[RW];
-            float sf[RW], mf[RW];
+            float sf[RW];
 #pragma unroll
             for (int j = 0; j < RW; ++j) {
                 cq[j] = wq[slot][j];
@@ -178,7 +191,6 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
                 sv[j] = (h2){sh, sh};
                 mv[j] = (h2){mh, mh};
                 sf[j] = (float)sh * kInvUnit;  // EPI: codes enter as c * 2^-20
-                mf[j] = (float)mh;
             }
             load_w(slot, g + DW);
             if constexpr (EPI) {
@@ -211,16 +223,12 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
                                                                              0, 0, 0);
                         }
                     }
-                    const f4 s0 = *reinterpret_cast<const f4*>(&xsum[buf][t][4 * q]);
-                    const f4 s1 = *reinterpret_cast<const f4*>(&xsum[buf][t + 1][4 * q]);
 #pragma unroll
                     for (int j = 0; j < RW; ++j)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             acc[j][t][i] = __builtin_fmaf(sf[j], c[j][0][i], acc[j][t][i]);
-                            acc[j][t][i] = __builtin_fmaf(mf[j], s0[i], acc[j][t][i]);
                             acc[j][t + 1][i] = __builtin_fmaf(sf[j], c[j][1][i], acc[j][t + 1][i]);
-                            acc[j][t + 1][i] = __builtin_fmaf(mf[j], s1[i], acc[j][t + 1][i]);
                         }
                 }
             } else {
@@ -247,9 +255,22 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
                 }
             }
             // the next group's activations: staged now, read after the barrier
-            stage_x((u + 1) % DX, buf ^ 1);
+            stage_x((u + 1) % DX, buf ^ 1, (g + 1) & 7);
             load_x((u + 1) % DX, g + 1 + DX);
             lds_barrier();
+        }
+        if constexpr (EPI) {
+            // The minimum term of the window's four groups on the matrix
+            // cores: y[tok][row] += sum over q of S_(g0+q)[tok] * min[row][g0+q],
+            // A = the tokens' group sums (token r, group q), B = the rows'
+            // minimums (group q, row r), fp32 operands.
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+                const float a = xsum[(g0 + q) & 7][t][r];
+#pragma unroll
+                for (int j = 0; j < RW; ++j)
+                    acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, mwin[j], acc[j][t], 0, 0, 0);
+            }
         }
     }
 
