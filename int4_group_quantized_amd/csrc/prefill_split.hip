@@ -32,9 +32,11 @@
 // denormals c * 2^-20) in the pair order of dequant_dword, A = the same 8
 // columns of token r of a token tile, permuted alike.  Output lane layout:
 // lane l holds tokens 4*(l/16)+i of weight row l%16.  In the EPI form each
-// group starts from a zero accumulator, and y += (scale * 2^20) * C_g and
-// y += min * S_g follow in fp32, with S_g of each output's token computed
-// once per round from the activation fragments and kept in LDS.
+// group starts from a zero accumulator and y += (scale * 2^20) * C_g follows
+// in fp32; the minimum term of the wave's (at most three) groups goes to the
+// matrix cores as one v_mfma_f32_16x16x4_f32 per token tile, A = S_g of the
+// tokens (computed once per round from the activation fragments, lane (r, q)
+// holding token r and group q), B = the row's minimums.
 #include "q4_device.hpp"
 #include "launch.hpp"
 
@@ -51,7 +53,6 @@ prefill_split_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restr
     extern __shared__ f4 lds_f4[];
     f4* part = lds_f4;                         // [2][NW][TT][64] partial sums per tile parity
     f4* tot = lds_f4 + 2 * NW * TT * 64;       // [kSplitMaxTiles][TT][64] totals of the slice
-    f4* gsum = tot + kSplitMaxTiles * TT * 64;  // EPI: [NW][GR][TT][64] per-token group sums
     constexpr int PER_ROUND = NW * GR;
 
     const int tid = threadIdx.x;
@@ -103,11 +104,15 @@ prefill_split_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restr
                 for (int s = 0; s < 4; ++s) xa[gi][s][t] = permute_window(xp[s]);
             }
         }
+        // EPI: the A operand of the minimum term, S_g of token r of each
+        // token tile for the wave's group q (zero for q >= GR): the lane's 32
+        // columns of token r, then the other three k-slots of the token
+        // (lanes r + 16j).
+        float sa[TT];
         if constexpr (EPI) {
-            // S_g for the tokens of this lane's outputs (4q + i of each token
-            // tile): the lane's 32 columns of token r, then the other three
-            // k-slots of the token (lanes r + 16j), then fetched by token.
             const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+            for (int t = 0; t < TT; ++t) sa[t] = 0.0f;
 #pragma unroll
             for (int gi = 0; gi < GR; ++gi)
 #pragma unroll
@@ -123,10 +128,7 @@ prefill_split_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restr
                     }
                     v = v + lane_swap16(v);
                     v = v + __shfl_xor(v, 32, 64);
-                    f4 sg;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sg[i] = __shfl(v, 4 * q + i, 64);
-                    gsum[((wave * GR + gi) * TT + t) * 64 + lane] = sg;
+                    sa[t] = q == gi ? v : sa[t];
                 }
         }
 
@@ -135,6 +137,7 @@ prefill_split_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restr
             f4 acc[TT];
 #pragma unroll
             for (int t = 0; t < TT; ++t) acc[t] = zero;
+            float bm = 0.0f;  // EPI: min of this lane's row for the wave's group q
 #pragma unroll
             for (int gi = 0; gi < GR; ++gi) {
                 const uint32_t keep = (uint32_t)__builtin_amdgcn_readfirstlane(-(int)(gw + gi < G));
@@ -142,7 +145,7 @@ prefill_split_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restr
                     // Exact codes as fp16 denormals c * 2^-20 (each nibble moved
                     // to mantissa bits 4..7), in the pair order of dequant_dword.
                     const float sf = f16_bits_to_f32((uint16_t)(ws[p][gi] & keep)) * kInvUnit;
-                    const float mf = f16_bits_to_f32((uint16_t)(wm[p][gi] & keep));
+                    bm = q == gi ? f16_bits_to_f32((uint16_t)(wm[p][gi] & keep)) : bm;
                     const u4 cw = wq[p][gi];
                     load_w(p, gi, rt + 2);
                     f4 cg[TT];
@@ -158,14 +161,9 @@ prefill_split_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restr
                                                                            s == 0 ? zero : cg[t], 0, 0, 0);
                     }
 #pragma unroll
-                    for (int t = 0; t < TT; ++t) {
-                        const f4 sg = gsum[((wave * GR + gi) * TT + t) * 64 + lane];
+                    for (int t = 0; t < TT; ++t)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            acc[t][i] = __builtin_fmaf(sf, cg[t][i], acc[t][i]);
-                            acc[t][i] = __builtin_fmaf(mf, sg[i], acc[t][i]);
-                        }
-                    }
+                        for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(sf, cg[t][i], acc[t][i]);
                 } else {
                     uint32_t wv[16];
                     weights_fp16(wq[p][gi], (uint16_t)(ws[p][gi] & keep), (uint16_t)(wm[p][gi] & keep), kc, wv);
@@ -180,6 +178,12 @@ prefill_split_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restr
                                                                             acc[t], 0, 0, 0);
                     }
                 }
+            }
+            if constexpr (EPI) {
+                // The minimum term of the wave's groups, sum over q of
+                // S_q[tok] * min_q[row], on the matrix cores (fp32 operands).
+#pragma unroll
+                for (int t = 0; t < TT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[t], bm, acc[t], 0, 0, 0);
             }
 #pragma unroll
             for (int t = 0; t < TT; ++t) part[((p * NW + wave) * TT + t) * 64 + lane] = acc[t];
@@ -222,7 +226,7 @@ template <int TT, int GR, bool EPI>
 static hipError_t launch_split(const GemvArgs& a, const uint16_t* X, float* Y, int m,
                                const DeviceInfo& dev, hipStream_t st) {
     constexpr int NW = kSplitWaves;
-    const size_t lds = ((size_t)2 * NW * TT + (size_t)kSplitMaxTiles * TT + (EPI ? (size_t)NW * GR * TT : 0)) * 64 *
+    const size_t lds = ((size_t)2 * NW * TT + (size_t)kSplitMaxTiles * TT) * 64 *
                        sizeof(f4);
     std::atomic<int>& attr_set = PerDevice<&prefill_split_kernel<TT, GR, NW, EPI>>::value[dev.device];
     if (attr_set.load(std::memory_order_acquire) == 0) {
