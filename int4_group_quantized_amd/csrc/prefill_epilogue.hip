@@ -22,11 +22,15 @@
 //    and turns it into 16 exact integer fp16 code pairs (dequant_dword),
 //    in the pair order (c0,c4) (c1,c5) (c2,c6) (c3,c7) of each dword;
 //  * the group's activations sit in a double-buffered LDS tile as permuted
-//    8-element windows (same pair order), and their per-token sums S_g in a
-//    small LDS array, both written one group ahead; one barrier per group;
+//    8-element windows (same pair order), and their per-token sums S_g in
+//    an LDS ring of eight groups, both written one group ahead; one barrier
+//    per group;
 //  * v_mfma_f32_16x16x32_f16 step s (0..3) contracts dword s of every
 //    lane's chunk; the first step of a group starts from a zero accumulator;
-//  * then y = fma(scale, C_g, y) and y = fma(min, S_g, y) per output, fp32.
+//  * then y = fma(scale, C_g, y) per output, fp32; every four groups the
+//    minimum term, sum over the four of min_g * S_g, is one
+//    v_mfma_f32_16x16x4_f32 per token tile (A = the tokens' sums S_g,
+//    B = the row's minimums).
 // Output lane layout of the 16x16 instruction: lane l holds rows 4*(l/16)+i
 // (tokens) of column l%16 (weight row).
 #include "q4_device.hpp"
@@ -51,9 +55,10 @@ prefill_epilogue_kernel(const uint8_t* __restrict__ packed, const uint16_t* __re
     constexpr int DX = TT <= 2 ? 3 : 2;
     constexpr int DW = TT <= 2 ? 6 : 4;    // a multiple of DX and of 2
     static_assert(DW % DX == 0 && DW % 2 == 0, "ring depths");
+    static_assert(DW == 4, "the minimum term runs on windows of four groups");
     static_assert(THREADS % 16 == 0, "the 16 windows of a token are one DPP row");
     __shared__ u4 xt[2][TOK][17];
-    __shared__ f4 xs[2][TOK / 4];          // S_g per token, 4 tokens per entry
+    __shared__ float xsr[8][TOK];          // S_g per token, groups g mod 8
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -105,17 +110,16 @@ prefill_epilogue_kernel(const uint8_t* __restrict__ packed, const uint16_t* __re
                 const float tot = reduce_lanes<16>(part);  // every lane of the DPP row gets the token's sum
                 if (w < WIN) {
                     xt[buf][w >> 4][w & 15] = v;
-                    if ((w & 15) == 0) reinterpret_cast<float*>(&xs[buf][0])[w >> 4] = tot;
+                    if ((w & 15) == 0) xsr[g & 7][w >> 4] = tot;
                 }
             }
         };
         u4 wq[DW];
-        uint16_t ws[DW], wm[DW];
+        uint16_t ws[DW];
         auto load_w = [&](int slot, int g) {
             const int gc = g < G ? g : G - 1;
             wq[slot] = __builtin_nontemporal_load(rp + gc * 4 + q);
             ws[slot] = srow[gc];
-            wm[slot] = mrow[gc];
         };
 #pragma unroll
         for (int d = 0; d < DW; ++d) load_w(d, d);
@@ -129,6 +133,10 @@ prefill_epilogue_kernel(const uint8_t* __restrict__ packed, const uint16_t* __re
         for (int t = 0; t < TT; ++t) y[t] = zero;
 
         for (int g0 = 0; g0 < Gp; g0 += DW) {
+            // This window's minimums, min[row][g0 + q] for lane (r, q) (zero
+            // past G), requested four groups before use.
+            const int gq = g0 + q;
+            const float mwin = f16_bits_to_f32((uint16_t)(mrow[gq < G ? gq : G - 1] & (uint32_t)(-(int)(gq < G))));
 #pragma unroll
             for (int u = 0; u < DW; ++u) {
                 const int g = g0 + u;
@@ -136,7 +144,6 @@ prefill_epilogue_kernel(const uint8_t* __restrict__ packed, const uint16_t* __re
                 // padded groups: zero scale and minimum (their activations are zero too)
                 const uint32_t keep = (uint32_t)__builtin_amdgcn_readfirstlane(-(int)(g < G));
                 const float sf = f16_bits_to_f32((uint16_t)(ws[u] & keep));
-                const float mf = f16_bits_to_f32((uint16_t)(wm[u] & keep));
                 h2 codes[16];
                 dequant_dword(wq[u].x, kc, codes + 0);
                 dequant_dword(wq[u].y, kc, codes + 4);
@@ -155,18 +162,18 @@ prefill_epilogue_kernel(const uint8_t* __restrict__ packed, const uint16_t* __re
                     }
                 }
 #pragma unroll
-                for (int t = 0; t < TT; ++t) {
-                    const f4 sg = xs[buf][t * 4 + q];
+                for (int t = 0; t < TT; ++t)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        y[t][i] = __builtin_fmaf(sf, acc[t][i], y[t][i]);
-                        y[t][i] = __builtin_fmaf(mf, sg[i], y[t][i]);
-                    }
-                }
+                    for (int i = 0; i < 4; ++i) y[t][i] = __builtin_fmaf(sf, acc[t][i], y[t][i]);
                 store_x(xr[(u + 1) % DX], buf ^ 1, g + 1);
                 load_x(xr[u % DX], g + DX);
                 lds_barrier();
             }
+            // The minimum term of the window on the matrix cores:
+            // y[tok][row] += sum over q of S_(g0+q)[tok] * min[row][g0+q].
+#pragma unroll
+            for (int t = 0; t < TT; ++t)
+                y[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsr[(g0 + q) & 7][t * 16 + r], mwin, y[t], 0, 0, 0);
         }
 
         if (store_row) {
