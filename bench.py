@@ -303,7 +303,8 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-forms", action="store_true", help="skip the extra forms")
-    ap.add_argument("--stack", action="store_true", help="also time the 36-layer, 108-GEMV stack")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the 36-layer, 108-GEMV stack on fresh weights per layer (a forms entry)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
@@ -465,8 +466,9 @@ def main():
     if not args.no_forms:
         forms["pages_stack_36x3_hidden2048_gemv_b1"] = time_pages_stack(torch, q4, dev, stream, f16)
         torch.cuda.empty_cache()
-    if args.stack:
+    if not args.no_forms and not args.no_stack:
         forms["stack_36x3_gemv_b1"] = time_stack(torch, q4, dev, stream, f16)
+        torch.cuda.empty_cache()
     if forms:
         result["forms"] = forms
 
