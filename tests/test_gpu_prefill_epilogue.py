@@ -46,6 +46,8 @@ def run(packed, s, m, X, dev):
                                       # K split over the waves (up to 48 tokens): three rounds with padded
                                       # groups, two tiles per workgroup, waves with no group
                                       (48, 300, 8192), (20, 8000, 384), (33, 2500, 640),
+                                      # 49 to 64 tokens with a last window of fewer than four groups
+                                      (56, 100, 640), (49, 70, 1152),
                                       # blocks of 128 tokens per workgroup (above 64 tokens): eight row
                                       # tiles per workgroup, four blocks, a partial block
                                       (193, 32768, 256), (500, 700, 640), (200, 3000, 1024),
@@ -79,7 +81,7 @@ def test_prefill_epilogue_fused(dev, mtok):
                  f"epilogue fused M={mtok}")
 
 
-@pytest.mark.parametrize("mtok", [1, 16, 34, 70, 200])
+@pytest.mark.parametrize("mtok", [1, 16, 34, 56, 70, 200])
 def test_prefill_epilogue_dyadic_bit_exact(dev, mtok):
     n, k, codes, scales, mins, _x = dyadic_case(mtok, 96, 384)
     X = np.random.Generator(np.random.PCG64(300 + mtok)).integers(-3, 4, (mtok, k)).astype(np.float16)
