@@ -250,14 +250,20 @@ static hipError_t launch_seg(const GemvArgs& a, const uint16_t* X, float* Y, int
     return hipGetLastError();
 }
 
-// Two passes per wave once one per wave would need more workgroups than CUs
-// (the staging buffers allow one workgroup per CU at 16 columns); four waves
-// per workgroup when that still needs no more workgroups than CUs.
+// One workgroup per CU (the staging buffers allow one at 16 columns) and one
+// pass per wave where possible: 4 waves per workgroup up to 4 passes per CU,
+// 8 up to 8, 12 up to 12; beyond, two passes per wave in 8-wave workgroups,
+// where each column read from LDS serves two rows.  At 8 to 12 passes per CU,
+// 12 waves of one pass measured 15-20% faster than 8 waves of two (3,072 x
+// 8,192 at B = 16: 17.3 against 20.8 us); at 16 passes per CU, 16 waves of one
+// were slower than 8 of two (4,096 x 11,008: 30.2 against 28.6 us).
 template <int LPR, int BT>
 static hipError_t launch_seg_rows(const GemvArgs& a, const uint16_t* X, float* Y, int nb, const DeviceInfo& dev,
                                   hipStream_t st) {
     constexpr int RPW = 64 / LPR;
     const long passes = ((long)a.n + RPW - 1) / RPW;
+    if (passes > (long)kSegWaves * dev.num_cu && passes <= 12L * dev.num_cu)
+        return launch_seg<LPR, BT, 1, 12>(a, X, Y, nb, dev, st);
     if (passes > (long)kSegWaves * dev.num_cu) return launch_seg<LPR, BT, 2, kSegWaves>(a, X, Y, nb, dev, st);
     if (passes <= (long)(kSegWaves / 2) * dev.num_cu) return launch_seg<LPR, BT, 1, kSegWaves / 2>(a, X, Y, nb, dev, st);
     return launch_seg<LPR, BT, 1, kSegWaves>(a, X, Y, nb, dev, st);
