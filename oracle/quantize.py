@@ -14,7 +14,11 @@ w = code * scale + min:
 
   1. per group, lo = min and hi = max of its 128 values;
   2. min   = fp16(lo), scale = fp16(fl32(hi - lo) / 15)   (15 = top code);
-     a zero minimum is stored as +0 (lo + 0 in fp32 turns -0 into +0);
+     a zero minimum is stored as +0.  The minimum of a group that holds
+     -0 (with or without +0) is the number zero, but which signed zero a
+     min-reduction returns depends on the order of its comparisons, so the
+     stored form is fixed to the canonical +0 (lo + 0 in fp32 turns -0
+     into +0);
   3. code  = clamp(round_half_even((w - min) / scale), 0, 15), computed
      against the STORED fp16 min and scale, so that the code is the nearest
      one under the dequantisation that will actually be applied;
@@ -30,7 +34,10 @@ fp16 minimum and scale are finite.
 
 Pins of this module (tests/test_oracle_quantize_pins.py) check it against
 exact rational arithmetic: exact round trips, the best code by brute force,
-the reconstruction error bound and the degenerate groups.
+the reconstruction error bound, the degenerate groups, a step-by-step
+emulation of the fp32 operations above (IEEE rounding written from its
+definition on rationals) over values placed on the code boundaries, and the
+signed-zero minimum.
 """
 from __future__ import annotations
 

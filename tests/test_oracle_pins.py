@@ -211,6 +211,33 @@ def pin_fp16_weights(orc):
             assert abs(Fraction(float(Y[b, r])) - exact_y) <= Fraction(2) ** -40
 
 
+def pin_term_magnitude(orc, seed=13):
+    """The error-bound magnitude T[b][n] = sum_k (code*scale + |min|) * |x_k|
+    against exact rational sums on tiny matrices.
+
+    Not a product of the method: it is the sum of the magnitudes of the terms
+    a kernel adds when it forms scale*sum(code*x) + min*sum(x) per group, the
+    quantity that the GPU tests scale by a multiple of 2^-24 to bound fp32
+    summation error.  Negative minimums and mixed-sign x make every plausible
+    slip visible (min without its absolute value, |w| instead of
+    code*scale + |min|, a dropped min term).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    for n, k in [(1, 128), (3, 256), (4, 384)]:
+        w = synth.draw_weights(rng, n, k)
+        X = synth.draw_activations(rng, 2, k)
+        T = orc.term_magnitude(orc.pack(w.codes), w.scales, w.mins, X)
+        assert T.shape == (2, n)
+        for b in range(2):
+            for r in range(n):
+                exact = Fraction(0)
+                for col in range(k):
+                    g = col // 128
+                    exact += ((int(w.codes[r, col]) * Fraction(float(w.scales[r, g]))
+                               + abs(Fraction(float(w.mins[r, g])))) * abs(Fraction(float(X[b, col]))))
+                assert abs(Fraction(float(T[b, r])) - exact) <= Fraction(2) ** -40 * exact, (n, k, b, r)
+
+
 PINS = [
     pin_brute_force,
     pin_closed_form_constant,
@@ -222,6 +249,7 @@ PINS = [
     pin_linearity,
     pin_known_answers,
     pin_fp16_weights,
+    pin_term_magnitude,
 ]
 
 
@@ -306,8 +334,26 @@ def _mutant_pack_order(mod):
     mod.pack = pack
 
 
+def _mutant_term_magnitude(formula):
+    def apply(mod):
+        orig_unpack = mod.unpack
+
+        def term_magnitude(packed, scales, mins, X):
+            X = np.asarray(X, dtype=np.float16).astype(np.float64)
+            k = X.shape[1]
+            c = orig_unpack(packed, k).astype(np.float64)
+            s = np.repeat(np.asarray(scales, np.float16).astype(np.float64), 128, axis=1)
+            m = np.repeat(np.asarray(mins, np.float16).astype(np.float64), 128, axis=1)
+            return np.abs(X) @ formula(c, s, m).T
+        mod.term_magnitude = term_magnitude
+    return apply
+
+
 MUTANTS = {
     "swapped_nibbles": _mutant_swapped_nibbles,
+    "term_magnitude_drops_min": _mutant_term_magnitude(lambda c, s, m: c * s),
+    "term_magnitude_signed_min": _mutant_term_magnitude(lambda c, s, m: c * s + m),
+    "term_magnitude_abs_weight": _mutant_term_magnitude(lambda c, s, m: np.abs(c * s + m)),
     "min_counted_four_times": _mutant_dequant(lambda c, s, m, *_: c * s + 4 * m),
     "min_sign": _mutant_dequant(lambda c, s, m, *_: c * s - m),
     "code_plus_one": _mutant_dequant(lambda c, s, m, *_: (c + 1) * s + m),

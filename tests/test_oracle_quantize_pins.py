@@ -186,12 +186,154 @@ def pin_export_bytes(orc):
     assert list(packed[0, :8]) == [0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]
 
 
+# --------------------------------------------------------------------------
+# IEEE rounding from its definition, on exact rationals (no NumPy arithmetic)
+# --------------------------------------------------------------------------
+
+def round_ieee(v: Fraction, p: int, emin: int, emax: int) -> Fraction:
+    """The binary floating-point number nearest to v, ties to the even
+    significand: p significand bits (the leading bit included), normal
+    exponents emin..emax, subnormals below 2^emin with spacing 2^(emin-p+1).
+    Overflow raises (the quantiser's inputs keep every step finite)."""
+    if v == 0:
+        return Fraction(0)
+    sign = -1 if v < 0 else 1
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    assert Fraction(2) ** e <= a < Fraction(2) ** (e + 1)
+    e = max(e, emin)
+    ulp = Fraction(2) ** (e - p + 1)
+    r = a / ulp
+    q = r.numerator // r.denominator
+    rem = r - q
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and q % 2 == 1):
+        q += 1
+    out = q * ulp
+    if out >= Fraction(2) ** (emax + 1):
+        raise OverflowError(float(v))
+    return sign * out
+
+
+def rn32(v: Fraction) -> Fraction:
+    return round_ieee(v, 24, -126, 127)
+
+
+def rn16(v: Fraction) -> Fraction:
+    return round_ieee(v, 11, -14, 15)
+
+
+def rne_int(v: Fraction) -> int:
+    q = v.numerator // v.denominator
+    rem = v - q
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and q % 2 == 1):
+        q += 1
+    return q
+
+
+def emulate_group_fp32(vals):
+    """One group through the quantiser's steps, each one correctly rounded
+    IEEE operation on exact rationals: span = fl32(hi - lo), scale =
+    fp16(fl32(span / 15)), min = fp16(lo) (a zero minimum of either sign is
+    the rational 0, i.e. +0), code = clamp(rne(fl32(fl32(w - min) / scale))),
+    code 0 where the stored scale is 0."""
+    lo, hi = min(vals), max(vals)
+    S = rn16(rn32(rn32(hi - lo) / 15))
+    M = rn16(lo)
+    if S == 0:
+        return [0] * len(vals), S, M
+    return [min(15, max(0, rne_int(rn32(rn32(w - M) / S)))) for w in vals], S, M
+
+
+def emulate_group_exact(vals, S, M):
+    """The same codes from the exact quotient (w - M) / S, no fp32 rounding."""
+    return [min(15, max(0, rne_int((w - M) / S))) for w in vals]
+
+
+def half_code_tie_rows(rng, n_rows: int) -> np.ndarray:
+    """float32 [n_rows][1024]: groups whose values sit on and within two fp32
+    ulps of the half-integers that separate codes.
+
+    Each group gets an fp16 scale S (dyadic in some rows, arbitrary in the
+    others) and an fp16 minimum M; values 0 and 1 are M and M + 15 S, so the
+    stored scale and minimum are S and M; the other 126 are the fp32 numbers
+    nearest to M + (c + 1/2) S for random c, moved by -2..2 ulps.  Here the
+    rounding of w - M and of the quotient decides codes: exact arithmetic
+    picks another code for some of them."""
+    k = 1024
+    W = np.empty((n_rows, k), np.float32)
+    for r in range(n_rows):
+        for j in range(k // 128):
+            if r % 2 == 0:
+                S = Fraction(2) ** -int(rng.integers(3, 12))
+                M = Fraction(-int(rng.integers(0, 257)), 128)
+            else:
+                S = Fraction(float(np.float16(rng.uniform(0.001, 0.05))))
+                M = -Fraction(float(np.float16(rng.uniform(0.0, 0.3))))
+            vals = [M, M + 15 * S]
+            for _ in range(126):
+                c = int(rng.integers(0, 15))
+                w = np.float32(float(rn32(M + (c + Fraction(1, 2)) * S)))
+                for _ in range(abs(int(rng.integers(-2, 3)))):
+                    w = np.nextafter(w, np.float32(np.inf) if rng.random() < 0.5 else np.float32(-np.inf))
+                vals.append(Fraction(float(w)))
+            for t, v in enumerate(vals):
+                W[r, 128 * j + t] = float(v)
+                assert Fraction(float(W[r, 128 * j + t])) == v
+    return W
+
+
+def pin_fp32_decision_steps(orc):
+    """Codes, scales and minimums equal a step-by-step emulation of the
+    stated fp32 operations in exact rational arithmetic, on groups built
+    around the code boundaries.  The data must also separate fp32 decisions
+    from exact ones (else it could not tell them apart): checked first."""
+    rng = np.random.Generator(np.random.PCG64(34))
+    W = half_code_tie_rows(rng, 6)
+    c, s, m = orc.quantize(W)
+    n, k = W.shape
+    differ = 0
+    for r in range(n):
+        for j in range(k // 128):
+            vals = [fr(v) for v in W[r, 128 * j:128 * (j + 1)]]
+            codes, S, M = emulate_group_fp32(vals)
+            differ += sum(a != b for a, b in zip(codes, emulate_group_exact(vals, S, M)))
+            assert fr(s[r, j]) == S and fr(m[r, j]) == M, (r, j)
+            assert list(c[r, 128 * j:128 * (j + 1)]) == codes, (r, j)
+    assert differ > 0, "tie set does not separate fp32 from exact decisions"
+
+
+def pin_signed_zero_minimum(orc):
+    """The minimum of a group that holds -0 (and maybe +0) is the rational
+    zero, whose sign depends on the order of comparisons: it is stored as +0
+    (bits 0x0000) whatever the order."""
+    W = np.zeros((1, 512), np.float32)
+    pos = np.linspace(0.01, 0.5, 128).astype(np.float32)
+    W[0, :128] = pos
+    W[0, 0] = -0.0                              # -0 first, positives after
+    W[0, 128:256] = pos
+    W[0, 255] = -0.0                            # -0 last
+    W[0, 256:384] = pos
+    W[0, 256], W[0, 257] = -0.0, 0.0            # both signs
+    W[0, 384:] = pos
+    W[0, 384], W[0, 511] = 0.0, -0.0
+    c, s, m = orc.quantize(W)
+    assert list(m.view(np.uint16)[0]) == [0, 0, 0, 0]
+    for j in range(4):
+        vals = [fr(v) for v in W[0, 128 * j:128 * (j + 1)]]
+        codes, S, _ = emulate_group_fp32(vals)
+        assert fr(s[0, j]) == S and list(c[0, 128 * j:128 * (j + 1)]) == codes
+
+
 PINS = [
     pin_exact_round_trip,
     pin_best_code_brute_force,
     pin_reconstruction_bound,
     pin_degenerate_groups,
     pin_export_bytes,
+    pin_fp32_decision_steps,
+    pin_signed_zero_minimum,
 ]
 
 
@@ -222,15 +364,16 @@ def _replace_quantize(body):
     return apply
 
 
-def _standard(grp, n, k, top=15, rnd=np.rint, group_of=128, use_stored=True, min_round=None, clamp=True):
+def _standard(grp, n, k, top=15, rnd=np.rint, group_of=128, use_stored=True, min_round=None, clamp=True,
+              wide=np.float32):
     g_n = k // group_of
-    grp = grp.reshape(n, g_n, group_of)
+    grp = grp.reshape(n, g_n, group_of).astype(wide)
     lo, hi = grp.min(axis=2), grp.max(axis=2)
-    s32 = (hi - lo) / np.float32(top)
+    s32 = (hi - lo) / wide(top)
     scales = s32.astype(np.float16)
-    mins = lo.astype(np.float16) if min_round is None else min_round(lo)
-    s = (scales.astype(np.float32) if use_stored else s32)[:, :, None]
-    m = (mins.astype(np.float32) if use_stored else lo)[:, :, None]
+    mins = (lo + wide(0)).astype(np.float16) if min_round is None else min_round(lo)
+    s = (scales.astype(wide) if use_stored else s32)[:, :, None]
+    m = (mins.astype(wide) if use_stored else lo)[:, :, None]
     with np.errstate(divide="ignore", invalid="ignore"):
         q = rnd((grp - m) / s)
     if clamp:
@@ -251,6 +394,9 @@ MUTANTS = {
         lambda grp, n, k: _standard(grp, n, k, min_round=lambda lo: np.trunc(lo * 1024) / 1024)),
     "no_clamp": _replace_quantize(lambda grp, n, k: _standard(grp, n, k, clamp=False)),
     "group_of_64": _replace_quantize(lambda grp, n, k: _standard(grp, n, k, group_of=64)),
+    "decisions_in_fp64": _replace_quantize(lambda grp, n, k: _standard(grp, n, k, wide=np.float64)),
+    "min_keeps_sign_of_zero": _replace_quantize(
+        lambda grp, n, k: _standard(grp, n, k, min_round=lambda lo: lo.astype(np.float16))),
 }
 
 
