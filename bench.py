@@ -233,6 +233,15 @@ def prefill_epilogue_launcher(q4, rot, X, Y, mtok):
 
 
 def cpu_model() -> str:
+    """CPU model name as lscpu reports it (falls back to /proc/cpuinfo)."""
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
@@ -243,47 +252,100 @@ def cpu_model() -> str:
     return platform.machine()
 
 
-def cpu_baseline(budget_s: float):
-    """The fp64 oracle, single-threaded, on row blocks of the fused workload.
+CPU_BLOCK = 1024  # rows per oracle call
+_CPU_CASE = None  # (packed, scales, mins, x) shared with forked workers
 
-    Blocks of 4,096 rows are processed in order, wrapping around, until the
-    time budget is used; the packed bytes are prepared outside the timing.
-    """
+
+def _one_blas_thread():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)  # for the rest of this worker process
+
+
+def _oracle_rows(r0: int) -> int:
     import oracle
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
+    packed, scales, mins, x = _CPU_CASE
+    r1 = min(packed.shape[0], r0 + CPU_BLOCK)
+    oracle.gemv(packed[r0:r1], scales[r0:r1], mins[r0:r1], x)
+    return r1 - r0
+
+
+def _time_blocks(fn, n_rows: int, budget_s: float):
+    """Call fn(r0) on CPU_BLOCK-row blocks in order, wrapping, until budget_s; (rows, seconds)."""
+    rows, t_total, r0 = 0, 0.0, 0
+    while t_total < budget_s:
+        t = time.perf_counter()
+        rows += fn(r0)
+        t_total += time.perf_counter() - t
+        r0 = 0 if r0 + CPU_BLOCK >= n_rows else r0 + CPU_BLOCK
+    return rows, t_total
+
+
+def cpu_baseline(budget_s: float):
+    """The fp64 NumPy oracle as it stands, on the GPU machine's host, before any GPU work.
+
+    Legs (the oracle is a reported baseline, not a target):
+      * all cores: 1,024-row blocks of the fused 25,088 x 3,072 matrix at B = 1,
+        spread over a pool of forked worker processes (one BLAS thread each),
+        one pass over the matrix per ~budget/3 s; this is `value`;
+      * one thread: the same blocks, in order, for ~budget/3 s;
+      * one thread, the small batch at B = 16 and the prompt at M = 34 tokens
+        on 1,024-row blocks of the same matrix (~budget/6 s each), scaled to
+        the whole matrix.
+    """
+    global _CPU_CASE
+    import multiprocessing as mp
+
+    import oracle
+    from threadpoolctl import threadpool_limits
     w, x = synth.workload("fused_25088x3072")
     packed = oracle.pack(w.codes)
-    block = 4096
-    rows_done = 0
-    t_total = 0.0
-    ctx = threadpool_limits(1) if threadpool_limits else None
-    if ctx:
-        ctx.__enter__()
-    try:
-        r0 = 0
-        while t_total < budget_s:
-            r1 = min(w.n, r0 + block)
-            t = time.perf_counter()
-            oracle.gemv(packed[r0:r1], w.scales[r0:r1], w.mins[r0:r1], x[0])
-            t_total += time.perf_counter() - t
-            rows_done += r1 - r0
-            r0 = 0 if r1 == w.n else r1
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
-    nbytes = algorithmic_bytes(rows_done, w.k, 1)
+    _CPU_CASE = (packed, w.scales, w.mins, x[0])
+    n, k = w.n, w.k
+
+    # one thread, B = 1
+    with threadpool_limits(1):
+        rows1, t1 = _time_blocks(_oracle_rows, n, budget_s / 3)
+    # all cores (the box's CPU share, at most 16 workers)
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    starts = list(range(0, n, CPU_BLOCK))
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores, initializer=_one_blas_thread) as pool:
+        pool.map(_oracle_rows, starts[:cores])  # workers up
+        passes, rows_p, t0 = 0, 0, time.perf_counter()
+        while passes == 0 or time.perf_counter() - t0 < budget_s / 3:
+            rows_p += sum(pool.map(_oracle_rows, starts, chunksize=1))
+            passes += 1
+        tp = time.perf_counter() - t0
+    # one thread, B = 16 and M = 34 on row blocks
+    X16 = synth.batch_activations(16)
+    X34 = synth.prefill_activations(34)
+    extra = {}
+    for name, X in (("small_batch_b16", X16), ("prefill_m34", X34)):
+        def blk(r0, X=X):
+            r1 = min(n, r0 + CPU_BLOCK)
+            oracle.gemm(packed[r0:r1], w.scales[r0:r1], w.mins[r0:r1], X)
+            return r1 - r0
+        with threadpool_limits(1):
+            rows_b, t_b = _time_blocks(blk, n, budget_s / 6)
+        extra[name] = {"us_per_call_full_matrix": round(t_b / rows_b * n * 1e6, 1),
+                       "GB_per_s": round(algorithmic_bytes(rows_b, k, X.shape[0]) / t_b / 1e9, 6),
+                       "sample": f"{rows_b} rows in {CPU_BLOCK}-row blocks, one thread, {t_b:.1f} s"}
+    _CPU_CASE = None
     return {
-        "value": round(nbytes / t_total / 1e9, 6),
+        "value": round(algorithmic_bytes(rows_p, k, 1) / tp / 1e9, 6),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"{rows_done} rows ({rows_done / w.n:.2f} passes) of the fused 25088x3072 matrix in "
-                  f"4096-row blocks, B=1, fp64 NumPy oracle, one thread, {t_total:.1f} s",
-        "us_per_call_full_matrix": round(t_total / rows_done * w.n * 1e6, 1),
+        "sample": f"{passes} pass(es) over the fused 25088x3072 matrix at B=1 in {CPU_BLOCK}-row blocks on "
+                  f"{cores} worker processes (one BLAS thread each), fp64 NumPy oracle, {tp:.1f} s",
+        "us_per_call_full_matrix": round(tp / rows_p * n * 1e6, 1),
+        "one_thread": {"GB_per_s": round(algorithmic_bytes(rows1, k, 1) / t1 / 1e9, 6),
+                       "us_per_call_full_matrix": round(t1 / rows1 * n * 1e6, 1),
+                       "sample": f"{rows1} rows in {CPU_BLOCK}-row blocks, {t1:.1f} s"},
+        "forms_one_thread": extra,
         "cpu": cpu_model(),
+        "cpus_visible": os.cpu_count(),
+        "numpy": np.__version__,
     }
 
 
@@ -313,6 +375,10 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the GEMV shards by rows: each GPU would run the same kernel on its row slice)", file=sys.stderr)
         sys.exit(2)
+
+    # The CPU baseline runs first, before the GPU is initialised: its
+    # all-cores leg forks worker processes.
+    cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
 
     import torch
     import int4_group_quantized_amd as q4
@@ -380,6 +446,9 @@ def main():
 
     forms = {}
     if not args.no_forms:
+        forms.update(time_diagnostics(torch, dev, stream, rot, xd, ms_eager))
+
+    if not args.no_forms:
         def gemv_form(name, batches=()):
             nn, kk, sd = synth.WORKLOADS[name]
             ww, xx = synth.gemv_case(nn, kk, sd)
@@ -416,8 +485,10 @@ def main():
                 "us_per_call": round(ms * 1e3, 3), "GB_per_s": round(bb / (ms * 1e-3) / 1e9, 1),
                 "frac_hbm": round(bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "speedup_vs_b_calls": round(b * ms_eager / ms, 3)}
-        for mtok in (34, 256):
-            X = f16(synth.prefill_activations(mtok))
+        # 16 tokens: the matrix-core forms at the batch where the small-batch
+        # path (bit-identical to batch 1) tops out, for the cost of that contract
+        for mtok in (16, 34, 256):
+            X = f16(synth.prefill_activations(mtok) if mtok != 16 else synth.batch_activations(16))
             Y = torch.empty((mtok, n), dtype=torch.float32, device=dev)
             ms = time_checked(torch, stream, prefill_launcher(q4, rot, X, Y, mtok), Y, 200, 5, 20)
             bb = algorithmic_bytes(n, k, mtok)
@@ -464,25 +535,65 @@ def main():
         del Ws, Wf, Pq, Sq, Mq
         torch.cuda.empty_cache()
     if not args.no_forms:
-        forms["pages_stack_36x3_hidden2048_gemv_b1"] = time_pages_stack(torch, q4, dev, stream, f16)
+        forms.update(time_pages_stack(torch, q4, dev, stream, f16))
         torch.cuda.empty_cache()
     if not args.no_forms and not args.no_stack:
-        forms["stack_36x3_gemv_b1"] = time_stack(torch, q4, dev, stream, f16)
+        forms.update(time_stack(torch, q4, dev, stream, f16))
         torch.cuda.empty_cache()
     if forms:
         result["forms"] = forms
 
-    if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
-        result["cpu_baseline"]["vs_gpu"] = round(gbs / result["cpu_baseline"]["value"], 1)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
+        result["cpu_baseline"]["vs_gpu"] = round(gbs / cpu["value"], 1)
 
     print(json.dumps(result), flush=True)
 
 
-def time_stack(torch, q4, dev, stream, f16):
-    """36 layers x (fused, o_proj, down) GEMVs, fresh weights per layer, one graph."""
-    shapes = [(synth.FUSED_N, synth.HIDDEN_K), (synth.OPROJ_N, synth.OPROJ_K), (synth.DOWN_N, synth.DOWN_K)]
+def step_forms(torch, q4, stream, name, calls, total, keep):
+    """Two forms of one decode step of independent projections `calls`
+    (tuples of q4g128_gemv arguments): the per-projection launches captured in
+    one graph, and one q4g128_gemv_grouped call (fewer, larger launches),
+    timed eager and from a graph.  The grouped outputs must equal the
+    per-projection outputs bit for bit."""
     lib = q4.library()
+
+    def launch_all(_i, st):
+        for c in calls:
+            rc = lib.q4g128_gemv(*c, st)
+            if rc != 0:
+                raise RuntimeError(q4.q4g128_status_string(rc))
+    ms, _reps, _ = time_graph(torch, stream, launch_all, 1, 20, 2)
+    ys = [k[-1] for k in keep]
+    torch.cuda.synchronize()
+    ref = [y.clone() for y in ys]
+    descs = (q4.GemvDesc * len(calls))(*[q4.GemvDesc(*c) for c in calls])
+
+    def launch_grouped(_i, st):
+        rc = lib.q4g128_gemv_grouped(descs, len(calls), st)
+        if rc != 0:
+            raise RuntimeError(q4.q4g128_status_string(rc))
+    for y in ys:
+        y.zero_()
+    ms_g_graph, _reps, _ = time_graph(torch, stream, launch_grouped, 1, 20, 2)
+    torch.cuda.synchronize()
+    if not all(torch.equal(a, b) for a, b in zip(ys, ref)):
+        raise RuntimeError(f"{name}: grouped outputs differ from the per-projection calls")
+    ms_g = time_eager(torch, stream, launch_grouped, 20, 2)
+    out = {}
+    for key, t, extra in ((name + "_gemv_b1", ms, {"launches": len(calls), "timing": "one graph"}),
+                          (name + "_grouped_b1", ms_g, {"timing": "eager, back-to-back calls",
+                                                       "us_per_step_graph": round(ms_g_graph * 1e3, 2),
+                                                       "bit_identical_to_per_projection": True})):
+        out[key] = {"us_per_step": round(t * 1e3, 2), "bytes": total,
+                    "GB_per_s": round(total / (t * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(total / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), **extra}
+    return out
+
+
+def time_stack(torch, q4, dev, stream, f16):
+    """36 layers x (fused, o_proj, down) GEMVs, fresh weights per layer."""
+    shapes = [(synth.FUSED_N, synth.HIDDEN_K), (synth.OPROJ_N, synth.OPROJ_K), (synth.DOWN_N, synth.DOWN_K)]
     calls = []
     keep = []
     total = 0
@@ -499,28 +610,20 @@ def time_stack(torch, q4, dev, stream, f16):
             calls.append((packed.data_ptr(), s.data_ptr(), m.data_ptr(), xx.data_ptr(), yy.data_ptr(), nn, kk))
             total += algorithmic_bytes(nn, kk, 1)
         print(f"stack: layer {layer} ready", file=sys.stderr, flush=True)
-
-    def launch_all(_i, st):
-        for c in calls:
-            rc = lib.q4g128_gemv(*c, st)
-            if rc != 0:
-                raise RuntimeError(q4.q4g128_status_string(rc))
-    ms, reps, _ = time_graph(torch, stream, launch_all, 1, 20, 2)
-    return {"us_per_step": round(ms * 1e3, 2), "launches": len(calls), "bytes": total,
-            "GB_per_s": round(total / (ms * 1e-3) / 1e9, 1),
-            "frac_hbm": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    out = step_forms(torch, q4, stream, "stack_36x3", calls, total, keep)
+    del keep
+    return out
 
 
 def time_pages_stack(torch, q4, dev, stream, f16):
     """The pages' decode step shape: 36 layers x (fused 25,088x2,048,
-    o_proj 2,048x2,048, down 2,048x11,008) GEMVs in one graph of 108 launches.
+    o_proj 2,048x2,048, down 2,048x11,008) GEMVs.
 
     One seeded weight set per shape is drawn on the host; every layer gets its
     own device copy of it (distinct memory, 1.4 GB in total, so the 256 MB
     Infinity Cache cannot serve one layer's weights to the next).
     """
     names = ["pages_fused_25088x2048", "pages_oproj_2048x2048", "pages_down_2048x11008"]
-    lib = q4.library()
     base = []
     for name in names:
         ww, xx = synth.workload(name)
@@ -536,19 +639,66 @@ def time_pages_stack(torch, q4, dev, stream, f16):
             calls.append((p2.data_ptr(), s2.data_ptr(), m2.data_ptr(), xx.data_ptr(), yy.data_ptr(), nn, kk))
             total += algorithmic_bytes(nn, kk, 1)
     torch.cuda.synchronize()
-
-    def launch_all(_i, st):
-        for c in calls:
-            rc = lib.q4g128_gemv(*c, st)
-            if rc != 0:
-                raise RuntimeError(q4.q4g128_status_string(rc))
-    ms, _reps, _ = time_graph(torch, stream, launch_all, 1, 20, 2)
-    out = {"us_per_step": round(ms * 1e3, 2), "launches": len(calls), "bytes": total,
-           "GB_per_s": round(total / (ms * 1e-3) / 1e9, 1),
-           "frac_hbm": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-           "weights": "one seeded set per shape, a device copy per layer"}
+    out = step_forms(torch, q4, stream, "pages_stack_36x3_hidden2048", calls, total, keep)
+    for v in out.values():
+        v["weights"] = "one seeded set per shape, a device copy per layer"
     del keep
     return out
+
+
+def time_diagnostics(torch, dev, stream, rot, xd, ms_gemv):
+    """Ceilings of the batch-1 GEMV on this device (libq4g128_diag.so):
+    its read-only twin on the same rotated weights, a plain streaming read of
+    the same byte count and of 8x it (rotated windows of a >= 512 MB pool,
+    so the Infinity Cache cannot serve them; the difference of the two gives
+    the steady read rate), and an empty kernel on the same grid."""
+    from int4_group_quantized_amd import diag
+    lib = diag.library()
+    out_buf = torch.empty(max(1, lib.q4diag_grid_waves()), dtype=torch.int32, device=dev)
+    op = out_buf.data_ptr()
+    ptrs = [(p.data_ptr(), s.data_ptr(), m.data_ptr()) for p, s, m in rot.sets]
+    R, n, k, xp = len(ptrs), rot.n, rot.k, xd.data_ptr()
+    nbytes = algorithmic_bytes(n, k, 1)
+
+    def twin(i, st):
+        p, s, m = ptrs[i % R]
+        if lib.q4diag_gemv_read_twin(p, s, m, xp, op, n, k, st) != 0:
+            raise RuntimeError("q4diag_gemv_read_twin failed")
+    forms = {}
+    ms_twin = time_eager(torch, stream, twin, 2000, 50)
+    forms["diag_read_twin_fused_25088x3072"] = {
+        "us_per_call": round(ms_twin * 1e3, 3), "GB_per_s": round(nbytes / (ms_twin * 1e-3) / 1e9, 1),
+        "frac_hbm": round(nbytes / (ms_twin * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "gemv_over_twin": round(ms_gemv / ms_twin, 4),
+        "what": "same grid, loads and addresses as the GEMV kernel, no arithmetic"}
+    win = -(-nbytes // 4096) * 4096
+    pool = torch.empty(max(MALL_DEFEAT_BYTES + 8 * win, 16 * win), dtype=torch.uint8, device=dev)
+    base = pool.data_ptr()
+    stream_ms = {}
+    for mult in (1, 8):
+        size = mult * win
+        nwin = pool.numel() // size
+
+        def read(i, st, size=size, nwin=nwin):
+            if lib.q4diag_stream_read(base + (i % nwin) * size, size, op, st) != 0:
+                raise RuntimeError("q4diag_stream_read failed")
+        ms = time_eager(torch, stream, read, 2000 if mult == 1 else 300, 20)
+        stream_ms[mult] = ms
+        forms[f"diag_stream_read_{size >> 20}MB"] = {
+            "bytes": size, "us_per_call": round(ms * 1e3, 3), "GB_per_s": round(size / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(size / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "windows_rotated": nwin}
+    steady = 7 * win / ((stream_ms[8] - stream_ms[1]) * 1e-3) / 1e9
+    forms["diag_steady_read"] = {"GB_per_s": round(steady, 1), "frac_hbm": round(steady / HBM_PEAK_GBS, 4),
+                                 "what": "(8x - 1x bytes) / (t_8x - t_1x) of the two streaming reads"}
+    del pool
+
+    def empty(_i, st):
+        if lib.q4diag_empty(st) != 0:
+            raise RuntimeError("q4diag_empty failed")
+    ms = time_eager(torch, stream, empty, 2000, 50)
+    forms["diag_empty_launch"] = {"us_per_call": round(ms * 1e3, 3),
+                                  "what": "back-to-back launches of an empty kernel on the GEMV's grid"}
+    return forms
 
 
 if __name__ == "__main__":

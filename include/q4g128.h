@@ -131,6 +131,43 @@ Q4_API q4_status q4g128_gemv(const uint8_t* packed, const uint16_t* scales,
                       int64_t n, int64_t k, void* stream);
 
 /*
+ * q4g128_gemv_grouped -- many independent batch-1 products in few launches:
+ *   for every i < count:  descs[i].y = W_i * descs[i].x   (as q4g128_gemv).
+ * The rumik write-up ("A detour: the laptop engine on an H100") measures a
+ * small projection at about one launch latency on a fast GPU and a decode
+ * step as launch-bound, and advises counting launches and issuing far fewer
+ * kernels per layer ("What I would tell someone starting this").  Here all
+ * projections whose K has the same pass mapping are streamed by one
+ * persistent launch of up to 32 projections; the projections are read from
+ * `descs` (a HOST array, read during the call and not kept).
+ *   descs[i]: packed, scales, mins, x, y, n, k with the layout, alignment and
+ *   limits of q4g128_gemv.
+ * Every y_i is bit-identical to q4g128_gemv on projection i (same lanes,
+ * chunk order and reductions per row).  The projections must be
+ * independent: no y_i may overlap any input of any projection or any other
+ * output (x and weights may be shared between projections).  The order in
+ * which projections execute is unspecified.
+ * Errors: Q4_EINVAL for descs == NULL, count < 1 or count above
+ * Q4G128_MAX_GROUPED, or any overlap above; every descriptor is checked as
+ * q4g128_gemv checks its arguments (first failing status returned), all
+ * before any HIP call.  Q4_EDEVICE: a launch failed; projections enqueued
+ * before it stay enqueued.
+ */
+typedef struct q4g128_gemv_desc {
+    const uint8_t* packed;   /* [n][k/2] */
+    const uint16_t* scales;  /* [n][k/128] fp16 */
+    const uint16_t* mins;    /* [n][k/128] fp16 */
+    const uint16_t* x;       /* [k] fp16 */
+    float* y;                /* [n] fp32, written in full */
+    int64_t n;
+    int64_t k;
+} q4g128_gemv_desc;
+
+#define Q4G128_MAX_GROUPED 65536
+
+Q4_API q4_status q4g128_gemv_grouped(const q4g128_gemv_desc* descs, int64_t count, void* stream);
+
+/*
  * q4g128_gemm_small_batch -- Y[b][n] = sum_k w[n][k] * X[b][k], 1 <= B <= 16.
  * Continuous request batching ("Adding GPU backends to a pure-C TTS engine:
  * Metal, CUDA, and the rented-Mac trick", batching passage): each weight row

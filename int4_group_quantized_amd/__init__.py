@@ -30,11 +30,19 @@ GROUP = 128
 MAX_K = 32768
 MAX_BATCH = 16
 INT8_MAX_K = 8192
+MAX_GROUPED = 65536
+
+
+class GemvDesc(ctypes.Structure):
+    """struct q4g128_gemv_desc of include/q4g128.h."""
+    _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("mins", ctypes.c_void_p),
+                ("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("n", ctypes.c_int64), ("k", ctypes.c_int64)]
 
 EXPORTED = (
     "q4g128_pack",
     "q4g128_quantize",
     "q4g128_gemv",
+    "q4g128_gemv_grouped",
     "q4g128_gemm_small_batch",
     "q4g128_gemm_prefill",
     "q4g128_gemm_prefill_epilogue",
@@ -64,11 +72,13 @@ def _load():
     lib.q4g128_pack.argtypes = [vp, vp, i64, i64, vp]
     lib.q4g128_quantize.argtypes = [vp, vp, vp, vp, i64, i64, vp]
     lib.q4g128_gemv.argtypes = [vp, vp, vp, vp, vp, i64, i64, vp]
+    lib.q4g128_gemv_grouped.argtypes = [ctypes.POINTER(GemvDesc), i64, vp]
     lib.q4g128_gemm_small_batch.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.q4g128_gemm_prefill.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.q4g128_gemv_int8.argtypes = [vp, vp, vp, vp, i64, i64, vp]
     lib.q4g128_gemm_prefill_epilogue.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
-    for name in ("q4g128_pack", "q4g128_quantize", "q4g128_gemv", "q4g128_gemm_small_batch", "q4g128_gemm_prefill",
+    for name in ("q4g128_pack", "q4g128_quantize", "q4g128_gemv", "q4g128_gemv_grouped", "q4g128_gemm_small_batch",
+                 "q4g128_gemm_prefill",
                  "q4g128_gemv_int8", "q4g128_gemm_prefill_epilogue"):
         getattr(lib, name).restype = ctypes.c_int32
     lib.q4g128_status_string.argtypes = [ctypes.c_int32]
@@ -178,6 +188,37 @@ def q4g128_gemv(packed, scales, mins, x, y=None, stream=None) -> torch.Tensor:
         _check(_lib.q4g128_gemv(packed.data_ptr(), scales.data_ptr(), mins.data_ptr(), x.data_ptr(),
                                 y.data_ptr(), n, k, _stream(dev, stream)), "q4g128_gemv")
     return y
+
+
+def gemv_descs(projections, ys):
+    """ctypes array of q4g128_gemv_desc for [(packed, scales, mins, x)] and outputs ys (shapes checked)."""
+    arr = (GemvDesc * len(projections))()
+    for i, ((packed, scales, mins, x), y) in enumerate(zip(projections, ys)):
+        n, k = _weights(packed, scales, mins)
+        _dev_tensor(x, f"x[{i}]", torch.float16, (k,))
+        _dev_tensor(y, f"y[{i}]", torch.float32, (n,))
+        _same_device(projections[0][0], packed, scales, mins, x, y)
+        arr[i] = GemvDesc(packed.data_ptr(), scales.data_ptr(), mins.data_ptr(), x.data_ptr(), y.data_ptr(), n, k)
+    return arr
+
+
+def q4g128_gemv_grouped(projections, ys=None, stream=None):
+    """[y_i = W_i x_i] for independent projections [(packed, scales, mins, x)], in few launches.
+
+    Each y_i is bit-identical to q4g128_gemv on projection i.  Returns the list of outputs.
+    """
+    projections = list(projections)
+    if not projections:
+        raise ValueError("projections must not be empty")
+    if ys is None:
+        ys = [torch.empty((p[0].shape[0],), dtype=torch.float32, device=p[0].device) for p in projections]
+    if len(ys) != len(projections):
+        raise ValueError("one output per projection")
+    arr = gemv_descs(projections, ys)
+    dev = projections[0][0].device
+    with torch.cuda.device(dev):
+        _check(_lib.q4g128_gemv_grouped(arr, len(projections), _stream(dev, stream)), "q4g128_gemv_grouped")
+    return ys
 
 
 def q4g128_gemm_small_batch(packed, scales, mins, X, Y=None, stream=None) -> torch.Tensor:

@@ -21,8 +21,13 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libq4g128.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+# Benchmark diagnostics (read-only GEMV twin, streaming read, empty launch):
+# a library of their own, outside the product ABI.
+DIAG_NAME = "libq4g128_diag.so"
+DIAG_PATH = os.path.join(PKG_DIR, DIAG_NAME)
+DIAG_SOURCES = ["diag.hip"]
 
-SOURCES = ["api.cpp", "gemv.hip", "gemv_seg.hip", "prefill.hip", "prefill_split.hip", "prefill_pair.hip", "prefill_epilogue.hip", "pack.hip",
+SOURCES = ["api.cpp", "gemv.hip", "gemv_group.hip", "gemv_seg.hip", "prefill.hip", "prefill_split.hip", "prefill_pair.hip", "prefill_epilogue.hip", "pack.hip",
            "quantize.hip", "head_int8.hip"]
 ARCH = "gfx950"
 
@@ -67,13 +72,10 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build_library(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, name: str, path: str, verbose: bool) -> None:
+    tmp = path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + [
-        f"-Wl,-soname,{LIB_NAME}",
+        f"-Wl,-soname,{name}",
         "-Wl,-rpath,/opt/rocm/lib",
     ]
     if verbose:
@@ -81,7 +83,17 @@ def build_library(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile and link libq4g128.so and the diagnostics library; returns the former's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + DIAG_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB_NAME, LIB_PATH, verbose)
+    _link([objs[s] for s in DIAG_SOURCES], DIAG_NAME, DIAG_PATH, verbose)
     return LIB_PATH
 
 

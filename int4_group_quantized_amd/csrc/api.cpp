@@ -5,7 +5,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
+#include <utility>
+#include <vector>
 
 #include "launch.hpp"
 
@@ -51,9 +54,14 @@ q4_status current_device(q4::DeviceInfo* out) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// End of [p, p + bytes), saturated at the top of the address space.
+uintptr_t end_of(const void* p, size_t bytes) {
+    const uintptr_t a = (uintptr_t)p;
+    return bytes > UINTPTR_MAX - a ? UINTPTR_MAX : a + bytes;
+}
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
-    return a0 < b0 + nb && b0 < a0 + na;
+    return (uintptr_t)a < end_of(b, nb) && (uintptr_t)b < end_of(a, na);
 }
 
 q4_status check_nk(int64_t n, int64_t k) {
@@ -74,7 +82,10 @@ q4_status check_product(const uint8_t* packed, const uint16_t* scales, const uin
         !aligned(Y, 4))
         return Q4_EALIGN;
     const size_t g = (size_t)(k / Q4G128_GROUP);
-    const size_t ybytes = (size_t)rows * (size_t)n * sizeof(float);
+    // rows and n are below 2^31, so their product fits; its byte count may not.
+    const uint64_t yelems = (uint64_t)rows * (uint64_t)n;
+    if (yelems > UINT64_MAX / sizeof(float)) return Q4_ESHAPE;
+    const size_t ybytes = (size_t)yelems * sizeof(float);
     if (overlaps(Y, ybytes, packed, (size_t)n * (size_t)k / 2) ||
         overlaps(Y, ybytes, scales, (size_t)n * g * 2) || overlaps(Y, ybytes, mins, (size_t)n * g * 2) ||
         overlaps(Y, ybytes, X, (size_t)rows * (size_t)k * 2))
@@ -134,6 +145,43 @@ q4_status q4g128_gemv(const uint8_t* packed, const uint16_t* scales, const uint1
     s = current_device(&dev);
     if (s != Q4_OK) return s;
     hipError_t e = q4::launch_gemv(make_args(packed, scales, mins, x, y, n, k), dev, (hipStream_t)stream);
+    return e == hipSuccess ? Q4_OK : device_error(e);
+}
+
+q4_status q4g128_gemv_grouped(const q4g128_gemv_desc* descs, int64_t count, void* stream) {
+    if (!descs || count < 1 || count > Q4G128_MAX_GROUPED) return Q4_EINVAL;
+    std::vector<q4::GemvArgs> list((size_t)count);
+    // Outputs must be pairwise disjoint and disjoint from every input.
+    std::vector<std::pair<uintptr_t, uintptr_t>> outs((size_t)count);
+    for (int64_t i = 0; i < count; ++i) {
+        const q4g128_gemv_desc& d = descs[i];
+        q4_status s = check_product(d.packed, d.scales, d.mins, d.x, d.y, d.n, d.k, 1);
+        if (s != Q4_OK) return s;
+        list[(size_t)i] = make_args(d.packed, d.scales, d.mins, d.x, d.y, d.n, d.k);
+        outs[(size_t)i] = {(uintptr_t)d.y, end_of(d.y, (size_t)d.n * sizeof(float))};
+    }
+    std::sort(outs.begin(), outs.end());
+    for (size_t i = 1; i < outs.size(); ++i)
+        if (outs[i - 1].second > outs[i].first) return Q4_EINVAL;
+    // The only output that can overlap [lo, hi) is the last one starting below hi.
+    auto hits_output = [&](const void* p, size_t bytes) {
+        const uintptr_t lo = (uintptr_t)p, hi = end_of(p, bytes);
+        auto it = std::lower_bound(outs.begin(), outs.end(), std::make_pair(hi, (uintptr_t)0));
+        if (it == outs.begin()) return false;
+        --it;
+        return it->second > lo;
+    };
+    for (int64_t i = 0; i < count; ++i) {
+        const q4g128_gemv_desc& d = descs[i];
+        const size_t g = (size_t)(d.k / Q4G128_GROUP);
+        if (hits_output(d.packed, (size_t)d.n * (size_t)d.k / 2) || hits_output(d.scales, (size_t)d.n * g * 2) ||
+            hits_output(d.mins, (size_t)d.n * g * 2) || hits_output(d.x, (size_t)d.k * 2))
+            return Q4_EINVAL;
+    }
+    q4::DeviceInfo dev;
+    q4_status s = current_device(&dev);
+    if (s != Q4_OK) return s;
+    hipError_t e = q4::launch_gemv_group(list.data(), (int)count, dev, (hipStream_t)stream);
     return e == hipSuccess ? Q4_OK : device_error(e);
 }
 

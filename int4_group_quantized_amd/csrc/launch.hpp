@@ -42,6 +42,21 @@ struct GemvArgs {
 
 int lanes_per_row(int k);
 
+// Projections of one grouped-GEMV launch (passed by value as the kernel
+// argument).  Projection i owns the global passes first[i] .. first[i+1]-1.
+constexpr int kGroupMax = 32;
+struct GroupTable {
+    const uint8_t* packed[kGroupMax];
+    const uint16_t* scales[kGroupMax];
+    const uint16_t* mins[kGroupMax];
+    const uint16_t* x[kGroupMax];
+    float* y[kGroupMax];
+    int n[kGroupMax];
+    int k[kGroupMax];
+    long first[kGroupMax + 1];
+    int count;
+};
+
 hipError_t launch_pack(const uint8_t* codes, uint8_t* packed, int64_t n, int64_t k, hipStream_t st);
 hipError_t launch_quantize(const float* W, uint8_t* packed, uint16_t* scales, uint16_t* mins, int64_t n,
                            int64_t k, hipStream_t st);
@@ -49,6 +64,10 @@ constexpr long kQuantizeMaxGroups = 0x7FFFFFFFL * 32L;  // grid limit of the exp
 hipError_t launch_head_int8(const int8_t* q, const uint16_t* scales, const uint16_t* x, float* y, int64_t n,
                             int64_t k, const DeviceInfo& dev, hipStream_t st);
 hipError_t launch_gemv(const GemvArgs& a, const DeviceInfo& dev, hipStream_t st);
+// Independent projections (no output overlaps any input or other output):
+// one launch per kGroupMax projections of the same pass mapping; shapes the
+// batch-1 GEMV runs on its batched kernel are launched one by one.
+hipError_t launch_gemv_group(const GemvArgs* list, int count, const DeviceInfo& dev, hipStream_t st);
 hipError_t launch_small_batch(const GemvArgs& a, const uint16_t* X, float* Y, int b,
                               const DeviceInfo& dev, hipStream_t st);
 // hipErrorNotSupported when the shape has no segmented form (LPR below 16, or

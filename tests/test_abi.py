@@ -41,6 +41,26 @@ def test_library_exports_every_declared_symbol():
     assert funcs == declared_symbols()
 
 
+DIAG_HEADER = os.path.join(ROOT, "include", "q4g128_diag.h")
+
+
+def test_diag_library_exports_its_header():
+    from int4_group_quantized_amd import diag
+    declared = sorted(set(re.findall(r"Q4DIAG_API\s+[\w\s\*]+?\b(q4diag_\w+)\s*\(", open(DIAG_HEADER).read())))
+    assert declared == sorted(diag.EXPORTED)
+    out = os.popen(f"nm -D --defined-only {diag.DIAG_PATH}").read()
+    assert sorted(line.split()[-1] for line in out.splitlines() if " T " in line) == declared
+    lib = diag.library()
+    assert lib.q4diag_gemv_read_twin(None, S, M, X, Y, 64, 3072, None) == -1
+    assert lib.q4diag_gemv_read_twin(P, S, M, X, Y, 64, 2048, None) == -2
+    assert lib.q4diag_stream_read(P, 100, Y, None) == -1
+    assert lib.q4diag_stream_read(P + 8, 1024, Y, None) == -1
+
+
+def test_every_header_is_covered():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["q4g128.h", "q4g128_diag.h"]
+
+
 def test_status_strings():
     for code in (OK, EINVAL, ESHAPE, EALIGN, q4.Q4_EDEVICE):
         s = q4.q4g128_status_string(code)
@@ -169,3 +189,40 @@ def test_python_binding_rejects_cpu_tensors():
     codes = torch.zeros((4, 128), dtype=torch.uint8)
     with pytest.raises(ValueError):
         q4.q4g128_pack(codes)
+
+
+def grouped(*descs, count=None):
+    arr = (q4.GemvDesc * max(1, len(descs)))(*[q4.GemvDesc(*d) for d in descs])
+    return q4.library().q4g128_gemv_grouped(arr if descs else None, len(descs) if count is None else count, None)
+
+
+def desc(i, p=None, s=None, m=None, x=None, y=None, n=64, k=256):
+    """Projection i of a fake group: its own 2^32-byte slot in each of the five regions."""
+    off = i << 32
+    return (P + off if p is None else p, S + off if s is None else s, M + off if m is None else m,
+            X + off if x is None else x, Y + off if y is None else y, n, k)
+
+
+def test_grouped_error_paths():
+    assert grouped() == EINVAL                                  # NULL descs
+    assert grouped(desc(0), count=0) == EINVAL
+    assert grouped(desc(0), count=-1) == EINVAL
+    assert grouped(desc(0), count=q4.MAX_GROUPED + 1) == EINVAL
+    assert grouped(desc(0), desc(1, k=200)) == ESHAPE           # one bad K
+    assert grouped(desc(0), desc(1, n=0)) == EINVAL
+    assert grouped(desc(0), desc(1, p=P + 8)) == EALIGN
+    assert grouped(desc(0), desc(1, y=Y + 2)) == EALIGN
+    assert grouped(desc(0), desc(1, y=Y + 64)) == EINVAL        # two outputs overlap
+    assert grouped(desc(0), desc(1, y=Y + 252)) == EINVAL       # overlap of one element (n = 64 floats)
+    assert grouped(desc(0), desc(1, x=Y)) == EINVAL             # an output is another projection's input
+    assert grouped(desc(0), desc(1, y=P + 128)) == EINVAL       # an output inside another's weights
+    assert grouped(desc(0), desc(1, y=M + 64)) == EINVAL        # ... inside another's minimums
+    assert grouped(desc(0), desc(1, y=X + 32)) == EINVAL        # ... over another's x
+
+
+def test_grouped_shared_inputs_pass_validation():
+    # x, weights and scales shared between projections are fine; n = 0 in the
+    # last descriptor makes the call fail validation before any HIP call.
+    assert grouped(desc(0), desc(1, x=X, p=P, s=S, m=M), desc(2, n=0)) == EINVAL
+    # adjacent outputs (y_1 starts where y_0 ends) do not overlap
+    assert grouped(desc(0), desc(1, y=Y + 256), desc(2, n=0)) == EINVAL
