@@ -654,7 +654,7 @@ def time_diagnostics(torch, dev, stream, rot, xd, ms_gemv):
     the steady read rate), and an empty kernel on the same grid."""
     from int4_group_quantized_amd import diag
     lib = diag.library()
-    out_buf = torch.empty(max(1, lib.q4diag_grid_waves()), dtype=torch.int32, device=dev)
+    out_buf = torch.zeros(lib.q4diag_out_words(), dtype=torch.int32, device=dev)
     op = out_buf.data_ptr()
     ptrs = [(p.data_ptr(), s.data_ptr(), m.data_ptr()) for p, s, m in rot.sets]
     R, n, k, xp = len(ptrs), rot.n, rot.k, xd.data_ptr()

@@ -188,9 +188,15 @@ Q4_API q4_status q4g128_gemm_small_batch(const uint8_t* packed, const uint16_t* 
  * Each weight is dequantised on chip to fp16, fp16(code*scale + min) with
  * one rounding, and contracted with the fp16 activations on the gfx950
  * matrix cores with fp32 accumulation.  M is a runtime argument (any
- * M >= 1, no re-specialisation per M).  Results agree with the exact
- * product to the fp16 rounding of w; they are not bit-identical to
- * q4g128_gemv.
+ * M >= 1, no re-specialisation per M).
+ * Accuracy contract: |Y - Y16| <= 256 * 2^-24 * sum_k |fp16(w) * x| where Y16
+ * is the exact product of the fp16-rounded weights; against the exact
+ * weights the error adds the rounding of each weight, up to 2^-11 * |w|.
+ * That term does not shrink with K: at short K (K = 128, one group per row)
+ * and millions of outputs a few outputs exceed a 2e-3 relative bound of the
+ * exact product (a few per 8 M outputs in tests).  Callers that need the
+ * exact-weight accuracy at every output use q4g128_gemm_prefill_epilogue,
+ * which keeps exact codes.  Results are not bit-identical to q4g128_gemv.
  *   X [M][K] fp16 -> Y [M][N] fp32.
  */
 Q4_API q4_status q4g128_gemm_prefill(const uint8_t* packed, const uint16_t* scales,

@@ -25,20 +25,21 @@ extern "C" {
 
 #define Q4DIAG_API __attribute__((visibility("default")))
 
-/* Waves in the grid of the kernels below (the batch-1 GEMV's grid at
-   K = 3,072): the number of uint32 words they write to `out`. */
-Q4DIAG_API int32_t q4diag_grid_waves(void);
+/* Size in uint32 words of the `out` buffer of the kernels below (their XOR
+   checksums; the twin returns -1 on a device whose GEMV grid has more waves). */
+Q4DIAG_API int32_t q4diag_out_words(void);
 
-/* Read-only twin of q4g128_gemv for K = 3,072: same arguments and loads as
-   the GEMV (weights [n][1536], scales and mins [n][24], x [3072]); writes
-   one XOR checksum per wave to out[q4diag_grid_waves()] instead of y. */
+/* Read-only twin of q4g128_gemv for K = 3,072: same arguments, grid and loads
+   as the GEMV (weights [n][1536], scales and mins [n][24], x [3072]); writes
+   one XOR checksum per wave to out[q4diag_out_words()] instead of y. */
 Q4DIAG_API int32_t q4diag_gemv_read_twin(const uint8_t* packed, const uint16_t* scales,
                                          const uint16_t* mins, const uint16_t* x, uint32_t* out,
                                          int64_t n, int64_t k, void* stream);
 
 /* Streaming read of `bytes` (a positive multiple of 16, 16-byte aligned
-   src) with 16-byte non-temporal loads on the GEMV's grid; one XOR
-   checksum per wave to out[q4diag_grid_waves()]. */
+   src) with 16-byte non-temporal loads, each word read once by a one-shot
+   grid of 1,024-thread blocks (two words per thread); a thread writes its
+   XOR checksum to out[q4diag_out_words()] only if it equals 0x9E3779B9. */
 Q4DIAG_API int32_t q4diag_stream_read(const void* src, int64_t bytes, uint32_t* out, void* stream);
 
 /* An empty kernel on the GEMV's grid. */

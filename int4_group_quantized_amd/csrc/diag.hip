@@ -10,16 +10,19 @@
 //     a CUDA kernel") builds exactly such a twin to separate the memory time of
 //     a GEMV from its arithmetic;
 //   * a plain streaming read of a byte range with 16-byte non-temporal loads
-//     on the same persistent grid (the achievable read rate for one launch of
-//     that size);
+//     (the achievable read rate for one launch of that size);
 //   * an empty kernel on the same grid (the back-to-back launch floor).
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 
 #include "q4g128_diag.h"
 #include "q4_device.hpp"
 #include "gemv_pass.hpp"
 
 namespace q4 {
+
+constexpr int kOutWords = 4096;  // checksum words: at least the waves of the GEMV grid on 256 CUs
 
 __device__ __forceinline__ uint32_t fold_wave(uint32_t v) {
 #pragma unroll
@@ -83,47 +86,56 @@ gemv_read_twin_kernel(const uint8_t* __restrict__ packed, const uint16_t* __rest
     if (lane == 0) out[(long)blockIdx.x * (blockDim.x >> 6) + wave] = acc;
 }
 
-// Grid-stride read of nvec 16-byte words, U loads in flight per thread.
-template <int U>
-__global__ void __launch_bounds__(kGemvThreads)
+// One-shot read: block b reads U * blockDim.x consecutive 16-byte words,
+// thread t words t, t + blockDim.x, ...; the grid covers the range once, so
+// the hardware dispatcher hands blocks to whichever CU frees up first.  Of
+// the grids measured for a 41 MB read (persistent 512 x 512 threads with 1 to
+// 16 loads in flight, one-shot blocks of 256 to 1,024 threads with 1 to 16
+// words each) this one was the fastest.
+constexpr int kStreamThreads = 1024;
+constexpr int kStreamWords = 2;
+
+__global__ void __launch_bounds__(kStreamThreads)
 stream_read_kernel(const u4* __restrict__ src, long nvec, uint32_t* __restrict__ out) {
-    const long stride = (long)gridDim.x * blockDim.x;
-    long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long base = (long)blockIdx.x * kStreamThreads * kStreamWords + threadIdx.x;
     uint32_t acc = 0;
-    for (; i + (U - 1) * stride < nvec; i += U * stride) {
-        u4 v[U];
+    u4 v[kStreamWords];
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+    for (int u = 0; u < kStreamWords; ++u) {
+        const long i = base + (long)u * kStreamThreads;
+        v[u] = i < nvec ? __builtin_nontemporal_load(src + i) : u4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-    }
-    for (; i < nvec; i += stride) {
-        const u4 v = __builtin_nontemporal_load(src + i);
-        acc ^= v.x ^ v.y ^ v.z ^ v.w;
-    }
-    acc = fold_wave(acc);
-    if ((threadIdx.x & 63) == 0) out[((long)blockIdx.x * blockDim.x + threadIdx.x) >> 6] = acc;
+    for (int u = 0; u < kStreamWords; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    // The loads must not be optimised away: a thread stores its checksum only
+    // when it equals a fixed value, which leaves the stores out in practice.
+    if (acc == 0x9E3779B9u) out[(((long)blockIdx.x * kStreamThreads + threadIdx.x) >> 6) % kOutWords] = acc;
 }
 
 __global__ void __launch_bounds__(kGemvThreads) empty_kernel() {}
 
-static int g_blocks_per_cu = 2;  // the GEMV's grid for K = 3,072: two 8-wave workgroups per CU
+constexpr int kBlocksPerCu = 2;  // the GEMV's grid for K = 3,072: two 8-wave workgroups per CU
+constexpr int kMaxDev = 64;
+static std::atomic<int> g_cu[kMaxDev];
 
+// The GEMV's grid on the current device (CU count queried once per device, so
+// that the launch costs of these diagnostics match the library's).
 static int grid_blocks() {
-    int dev = 0, cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return -1;
-    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-    return cu * g_blocks_per_cu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return -1;
+    int cu = g_cu[dev].load(std::memory_order_relaxed);
+    if (cu == 0) {
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+        g_cu[dev].store(cu, std::memory_order_relaxed);
+    }
+    return cu * kBlocksPerCu;
 }
 
 }  // namespace q4
 
 extern "C" {
 
-int32_t q4diag_grid_waves(void) {
-    const int g = q4::grid_blocks();
-    return g < 0 ? -1 : g * (q4::kGemvThreads / 64);
-}
+int32_t q4diag_out_words(void) { return q4::kOutWords; }
 
 int32_t q4diag_gemv_read_twin(const uint8_t* packed, const uint16_t* scales, const uint16_t* mins,
                               const uint16_t* x, uint32_t* out, int64_t n, int64_t k, void* stream) {
@@ -132,6 +144,7 @@ int32_t q4diag_gemv_read_twin(const uint8_t* packed, const uint16_t* scales, con
     constexpr int LPR = 32, CPL = 3, RPW = 64 / LPR;
     const int blocks = q4::grid_blocks();
     if (blocks < 0) return -4;
+    if ((long)blocks * (q4::kGemvThreads / 64) > q4::kOutWords) return -1;
     const long passes = (n + RPW - 1) / RPW;
     long grid = blocks;
     const long need = (passes + 7) / 8;
@@ -143,10 +156,12 @@ int32_t q4diag_gemv_read_twin(const uint8_t* packed, const uint16_t* scales, con
 
 int32_t q4diag_stream_read(const void* src, int64_t bytes, uint32_t* out, void* stream) {
     if (!src || !out || bytes <= 0 || bytes % 16 != 0 || ((uintptr_t)src & 15) != 0) return -1;
-    const int blocks = q4::grid_blocks();
-    if (blocks < 0) return -4;
-    hipLaunchKernelGGL((q4::stream_read_kernel<4>), dim3((unsigned)blocks), dim3(q4::kGemvThreads), 0,
-                       (hipStream_t)stream, reinterpret_cast<const q4::u4*>(src), (long)(bytes / 16), out);
+    const long nvec = bytes / 16;
+    const long per = (long)q4::kStreamThreads * q4::kStreamWords;
+    const long blocks = (nvec + per - 1) / per;
+    if (blocks > 0x7FFFFFFFL) return -1;
+    hipLaunchKernelGGL(q4::stream_read_kernel, dim3((unsigned)blocks), dim3(q4::kStreamThreads), 0,
+                       (hipStream_t)stream, reinterpret_cast<const q4::u4*>(src), nvec, out);
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

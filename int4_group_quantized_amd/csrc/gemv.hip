@@ -277,7 +277,10 @@ gemm_batched_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
     const int wave = tid >> 6;
     const int j = lane % LPR;
     const int rsub = lane / LPR;
-    const int CPL = (C + LPR - 1) / LPR;  // ragged rows: lanes skip chunks past C
+    // Ragged rows: a lane's chunk past C loads the row's last chunk (in range)
+    // and meets zero activations and a zero chunk sum, as in gemv_reg_kernel,
+    // so that every lane applies the same group updates in the same order.
+    const int CPL = (C + LPR - 1) / LPR;
     const long passes = ((long)n + RPW - 1) / RPW;
     const long p0 = ((long)blockIdx.x * (blockDim.x >> 6) + wave) * (long)ppw;
 
@@ -292,8 +295,10 @@ gemm_batched_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
 #pragma unroll
         for (int b = 0; b < BT; ++b) yl[b] = 0.0f;
         for (int t = 0; t < CPL; ++t) {
-            const int c = j + t * LPR;
-            if (c >= C) break;
+            const int c0 = j + t * LPR;
+            const bool valid = c0 < C;
+            const int c = valid ? c0 : C - 1;
+            const uint32_t keep = valid ? 0xFFFFFFFFu : 0u;
             const u4 q = __builtin_nontemporal_load(rp + c);
             const uint16_t s = scales[gbase + (c >> 2)];
             const uint16_t m = mins[gbase + (c >> 2)];
@@ -305,13 +310,13 @@ gemm_batched_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
                     const u4 v = xq[((size_t)b * 4 + d) * C + c];
-                    xp[4 * d + 0] = as_h2(v.x);
-                    xp[4 * d + 1] = as_h2(v.y);
-                    xp[4 * d + 2] = as_h2(v.z);
-                    xp[4 * d + 3] = as_h2(v.w);
+                    xp[4 * d + 0] = as_h2(v.x & keep);
+                    xp[4 * d + 1] = as_h2(v.y & keep);
+                    xp[4 * d + 2] = as_h2(v.z & keep);
+                    xp[4 * d + 3] = as_h2(v.w & keep);
                 }
                 const float dot = chunk_dot(codes, xp);
-                yl[b] = group_update(yl[b], s, m, dot, xsum[b * C + c]);
+                yl[b] = group_update(yl[b], s, m, dot, valid ? xsum[b * C + c] : 0.0f);
             }
         }
 #pragma unroll

@@ -11,7 +11,7 @@ import torch  # noqa: F401  (loads torch's HIP runtime before the library binds 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 DIAG_PATH = os.path.join(_PKG_DIR, "libq4g128_diag.so")
 
-EXPORTED = ("q4diag_grid_waves", "q4diag_gemv_read_twin", "q4diag_stream_read", "q4diag_empty")
+EXPORTED = ("q4diag_out_words", "q4diag_gemv_read_twin", "q4diag_stream_read", "q4diag_empty")
 
 
 def _load():
@@ -19,7 +19,7 @@ def _load():
         raise ImportError(f"{DIAG_PATH} is missing: build it with `python int4_group_quantized_amd/build.py`")
     lib = ctypes.CDLL(DIAG_PATH)
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
-    lib.q4diag_grid_waves.argtypes = []
+    lib.q4diag_out_words.argtypes = []
     lib.q4diag_gemv_read_twin.argtypes = [vp, vp, vp, vp, vp, i64, i64, vp]
     lib.q4diag_stream_read.argtypes = [vp, i64, vp, vp]
     lib.q4diag_empty.argtypes = [vp]

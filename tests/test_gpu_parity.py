@@ -148,7 +148,11 @@ def test_gemv_zero_and_scaling(dev):
 @pytest.mark.parametrize("n,k", [(25088, 3072), (3072, 8192), (257, 512), (100, 11008), (33, 384), (9, 32768),
                                  (2048, 11008), (300, 2176), (64, 12160), (50, 12416),
                                  (130, 5120), (70, 5632), (33, 7168), (2100, 11008), (4500, 5120), (8300, 5632),
-                                 (1, 11008), (5, 2048), (3, 1024)])
+                                 (1, 11008), (5, 2048), (3, 1024),
+                                 # more passes than one round of the grid, with every column in LDS:
+                                 # the batched kernel (ragged rows at K = 2,176 and, for B <= 4,
+                                 # 11,008; 64 lanes of three chunks at 6,144)
+                                 (4200, 2176), (4500, 11008), (5000, 6144)])
 def test_small_batch_bit_identical_to_gemv(dev, n, k):
     w = synth.weights(n, k, seed=n + k)
     packed, s, m = upload(w, dev, q4)
@@ -158,6 +162,22 @@ def test_small_batch_bit_identical_to_gemv(dev, n, k):
     for b in range(1, 17):
         Y = cpu(q4.q4g128_gemm_small_batch(packed, s, m, Xd[:b].contiguous()))
         assert np.array_equal(Y, singles[:b]), f"B={b}: batched rows differ from the batch-1 call"
+
+
+@pytest.mark.parametrize("n,k", [(4200, 2176), (4500, 11008), (300, 2176)])
+def test_small_batch_infinite_last_scale(dev, n, k):
+    """Ragged rows whose last group has an infinite scale or minimum: every
+    kernel feeds a ragged lane's missing chunk zero activations, so the
+    result (NaN where inf * 0 occurs) is the batch-1 call's in every column."""
+    w = synth.weights(n, k, seed=n + 3 * k)
+    w.scales[::7, -1] = np.float16(np.inf)
+    w.mins[3::11, -1] = np.float16(-np.inf)
+    packed, s, m = upload(w, dev, q4)
+    Xd = to_dev_f16(synth.activations(4, k, seed=5), dev)
+    singles = np.stack([cpu(q4.q4g128_gemv(packed, s, m, Xd[b].contiguous())) for b in range(4)])
+    for b in (2, 4):
+        Y = cpu(q4.q4g128_gemm_small_batch(packed, s, m, Xd[:b].contiguous()))
+        assert np.array_equal(Y.view(np.uint32), singles[:b].view(np.uint32)), f"B={b}"
 
 
 @pytest.mark.parametrize("b", [2, 4, 8, 16])
@@ -251,6 +271,31 @@ def test_prefill_parity_fused(dev, mtok):
     assert_rel(Y, oracle.gemm(packed_np, w.scales, w.mins, X), f"prefill M={mtok}")
     assert_bound(Y, oracle.gemm_fp16_weights(packed_np, w.scales, w.mins, X),
                  prefill_bound_T(packed_np, w, X), 256, f"prefill fp16-w M={mtok}")
+
+
+def test_prefill_fp16_weights_short_k_bound(dev):
+    """K = 128 (one group per row), 256 tokens x 32,768 rows: the short-K case
+    where rounding each weight to fp16 is largest against the product.  Every
+    output must be within 256 * 2^-24 * sum|fp16(w) x| of the exact product of
+    the fp16 weights (the contract of q4g128_gemm_prefill).  Against the exact
+    weights a few outputs may exceed 2e-3 * (|y| + rms): the count is
+    reported, and the epilogue form, which keeps exact codes, must have none."""
+    mtok, n, k = 256, 32768, 128
+    w = synth.weights(n, k, seed=128256)
+    X = synth.activations(mtok, k, seed=128257)
+    packed_np = oracle.pack(w.codes)
+    packed, s, m = upload(w, dev, q4)
+    Xd = to_dev_f16(X, dev)
+    Y = cpu(q4.q4g128_gemm_prefill(packed, s, m, Xd))
+    assert_bound(Y, oracle.gemm_fp16_weights(packed_np, w.scales, w.mins, X),
+                 prefill_bound_T(packed_np, w, X), 256, "prefill fp16-w K=128")
+    ref = oracle.gemm(packed_np, w.scales, w.mins, X)
+    rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
+    over = int((np.abs(Y - ref) > 2e-3 * (np.abs(ref) + rms)).sum())
+    note(f"[gpu-test]   fp16-weight prefill, K=128: {over} of {Y.size} outputs beyond 2e-3*(|y|+rms) "
+         f"of the exact product (allowed by its contract)")
+    Ye = cpu(q4.q4g128_gemm_prefill_epilogue(packed, s, m, Xd))
+    assert_rel(Ye, ref, "epilogue K=128")
 
 
 # --------------------------------------------------------------------------

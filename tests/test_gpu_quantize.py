@@ -113,16 +113,15 @@ def test_quantize_half_code_ties(dev):
     assert (codes % 2 == 0).sum() > 0 and (codes % 2 == 1).sum() > 0
 
 
-def test_quantize_full_size_sampled(dev):
-    """The fused 25,088 x 3,072 projection in the benchmark's launch: sampled
-    rows bit-exact against the oracle, every element within the reconstruction
+def test_quantize_full_size(dev):
+    """The fused 25,088 x 3,072 projection in the benchmark's launch: every
+    row bit-exact against the oracle, every element within the reconstruction
     bound, and a repeated call bitwise identical."""
     n, k = synth.FUSED_N, synth.HIDDEN_K
     W = synth.float_weights(n, k, synth.SEEDS["float_weights"])
     Wd = torch.from_numpy(W).to(dev)
     p1, s1, m1 = (cpu(t) for t in q4.q4g128_quantize(Wd))
-    rows = np.unique(np.concatenate([np.arange(0, n, 97), [n - 1]]))
-    assert_same((p1, s1.view(np.uint16), m1.view(np.uint16)), W, rows)
+    assert_same((p1, s1.view(np.uint16), m1.view(np.uint16)), W)
     # reconstruction bound at full size (oracle-free property)
     codes = oracle.unpack(p1, k).astype(np.float64)
     S = np.repeat(s1.astype(np.float64), 128, axis=1)
