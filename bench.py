@@ -9,9 +9,13 @@ back on the benchmark's stream, bracketed by HIP events on that stream; the
 same launches replayed from a HIP graph are timed as a cross-check that must
 reproduce the eager output.
 
-Prints ONE JSON line.  Extra forms (other shapes, small batch, prompt
-processing, the int8 output head, the export quantiser, the pages' 108-launch
-step and the 36-layer stack) are reported under "forms".
+Prints ONE JSON line.  Extra forms (the GEMV's ceilings from the diagnostics
+library: its read-only twin, a plain streaming read and an empty launch;
+other shapes, small batch, prompt processing, the int8 output head, the
+export quantiser, and the pages' and the 36-layer decode steps as 108
+launches and as grouped calls) are reported under "forms".  The CPU oracle is
+timed first, before the GPU is initialised, on one thread and on all the
+host's cores (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -36,7 +40,8 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak of the MI355X
 MALL_DEFEAT_BYTES = 512 << 20
 GRAPH_LAUNCHES = 100
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_fused_25088x3072.json")
-KERNEL_SOURCES = ["int4_group_quantized_amd/csrc/gemv.hip", "int4_group_quantized_amd/csrc/q4_device.hpp"]
+KERNEL_SOURCES = ["int4_group_quantized_amd/csrc/gemv.hip", "int4_group_quantized_amd/csrc/gemv_pass.hpp",
+                  "int4_group_quantized_amd/csrc/q4_device.hpp"]
 
 
 def algorithmic_bytes(n: int, k: int, b: int = 1) -> int:
