@@ -16,7 +16,8 @@
 // few projections; for each "segment" (the part of the range inside one
 // projection) the workgroup stages that projection's x once in LDS, every
 // lane copies its slice into registers, and the waves run the batch-1 pass
-// loop with two passes of weights in flight.
+// loop with the batch-1 kernel's number of passes in flight (one at
+// K = 3,072, two elsewhere).
 //
 // Every row goes through compute_pass<LPR, CPL> with the same lanes, chunk
 // order, group updates and butterfly as gemv_reg_kernel for its K, so every
@@ -27,7 +28,7 @@
 
 namespace q4 {
 
-template <int LPR, int CPL, bool RAGGED>
+template <int LPR, int CPL, bool RAGGED, int D>
 __global__ void __launch_bounds__(kGemvThreads)
 gemv_group_kernel(const GroupTable tab) {
     constexpr int RPW = 64 / LPR;
@@ -65,7 +66,7 @@ gemv_group_kernel(const GroupTable tab) {
 
         PassLoad<CPL> A, B;
         if (p < pend) load_pass<LPR, CPL, RAGGED>(A, packed, scales, mins, clamp(row_of(p)), k, j);
-        if (p + NW < pend) load_pass<LPR, CPL, RAGGED>(B, packed, scales, mins, clamp(row_of(p + NW)), k, j);
+        if (D == 2 && p + NW < pend) load_pass<LPR, CPL, RAGGED>(B, packed, scales, mins, clamp(row_of(p + NW)), k, j);
 
         // Every wave has copied the previous segment's x into registers.
         if (staged) lds_barrier();
@@ -77,6 +78,14 @@ gemv_group_kernel(const GroupTable tab) {
         float xs[CPL];
         lane_activations<LPR, CPL, RAGGED>(x_lds, C, j, xp, xs);
 
+        if constexpr (D == 1) {
+            while (p < pend) {
+                compute_pass<LPR, CPL>(A, xp, xs, y, row_of(p), n, j);
+                p += NW;
+                if (p < pend) load_pass<LPR, CPL, RAGGED>(A, packed, scales, mins, clamp(row_of(p)), k, j);
+            }
+            continue;
+        }
         while (p < pend) {
             compute_pass<LPR, CPL>(A, xp, xs, y, row_of(p), n, j);
             if (p + 2 * NW < pend)
@@ -95,17 +104,17 @@ gemv_group_kernel(const GroupTable tab) {
 // Host side
 // ---------------------------------------------------------------------------
 
-template <int LPR, int CPL, bool RAGGED>
+template <int LPR, int CPL, bool RAGGED, int D>
 static hipError_t launch_group_table(const GroupTable& tab, int max_k, const DeviceInfo& dev, hipStream_t st) {
     constexpr int kThreads = kGemvThreads;
     const size_t lds = (size_t)max_k * 2;
-    std::atomic<int>& cached = PerDevice<&gemv_group_kernel<LPR, CPL, RAGGED>>::value[dev.device];
+    std::atomic<int>& cached = PerDevice<&gemv_group_kernel<LPR, CPL, RAGGED, D>>::value[dev.device];
     int per_cu = cached.load(std::memory_order_relaxed);
     if (per_cu == 0) {
         int nb = 0;
         // The largest x this instantiation stages: K = 32 * LPR * CPL.
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &nb, reinterpret_cast<const void*>(&gemv_group_kernel<LPR, CPL, RAGGED>), kThreads,
+            &nb, reinterpret_cast<const void*>(&gemv_group_kernel<LPR, CPL, RAGGED, D>), kThreads,
             (size_t)64 * LPR * CPL);
         if (e != hipSuccess) return e;
         per_cu = nb > 0 ? nb : 1;
@@ -115,7 +124,7 @@ static hipError_t launch_group_table(const GroupTable& tab, int max_k, const Dev
     long grid = (long)dev.num_cu * per_cu;
     const long need = (total + (kThreads / 64) - 1) / (kThreads / 64);
     if (grid > need) grid = need;
-    hipLaunchKernelGGL((gemv_group_kernel<LPR, CPL, RAGGED>), dim3((unsigned)grid), dim3(kThreads), lds, st, tab);
+    hipLaunchKernelGGL((gemv_group_kernel<LPR, CPL, RAGGED, D>), dim3((unsigned)grid), dim3(kThreads), lds, st, tab);
     return hipGetLastError();
 }
 
@@ -145,8 +154,10 @@ int group_variant(int k) {
 
 static hipError_t dispatch_group(int v, const GroupTable& tab, int max_k, const DeviceInfo& dev, hipStream_t st) {
     switch (v) {
+// The passes in flight per wave follow the batch-1 GEMV's choice (one at
+// K = 3,072, two elsewhere).
 #define Q4_GRP(I, L, P, R) \
-    case I: return launch_group_table<L, P, R>(tab, max_k, dev, st);
+    case I: return launch_group_table<L, P, R, (L == 32 && P == 3 && !R) ? 1 : 2>(tab, max_k, dev, st);
         Q4_GRP(0, 64, 1, false) Q4_GRP(1, 64, 2, false) Q4_GRP(2, 64, 3, false) Q4_GRP(3, 64, 4, false)
         Q4_GRP(4, 32, 1, false) Q4_GRP(5, 32, 2, false) Q4_GRP(6, 32, 3, false) Q4_GRP(7, 16, 1, false)
         Q4_GRP(8, 16, 3, false) Q4_GRP(9, 8, 1, false) Q4_GRP(10, 8, 3, false) Q4_GRP(11, 4, 1, false)
