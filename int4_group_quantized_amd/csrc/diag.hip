@@ -3,9 +3,9 @@
 // them is part of the product; bench.py times them beside the GEMV.
 //
 //   * a read-only twin of the batch-1 GEMV kernel for K = 3,072 (32 lanes per
-//     row, 3 chunks per lane): the same grid, pass walk, two passes in
-//     flight, weight, scale, minimum and activation loads with the same
-//     addresses, and no arithmetic: every loaded word is XOR-folded into one
+//     row, 3 chunks per lane): the same grid, pass walk and pass schedule,
+//     weight, scale, minimum and activation loads with the same addresses,
+//     and no arithmetic: every loaded word is XOR-folded into one
 //     value per wave.  The rumik write-up ("Step 7: why the GEMV was stuck, and
 //     a CUDA kernel") builds exactly such a twin to separate the memory time of
 //     a GEMV from its arithmetic;
@@ -57,9 +57,11 @@ gemv_read_twin_kernel(const uint8_t* __restrict__ packed, const uint16_t* __rest
     auto row_of = [&](long pp) { return (int)(pp * RPW) + rsub; };
     auto clamp = [&](int r) { return r < n ? r : n - 1; };
 
+    // The GEMV's schedule at this K: the next pass is requested before the
+    // current one is consumed.
+    static_assert(pass_schedule(LPR, CPL, false) == kPassNextFirst, "twin follows the GEMV's schedule");
     PassLoad<CPL> A, B;
     if (p < passes) load_pass<LPR, CPL>(A, packed, scales, mins, clamp(row_of(p)), k, j);
-    if (p + W < passes) load_pass<LPR, CPL>(B, packed, scales, mins, clamp(row_of(p + W)), k, j);
     stage_x<LPR, CPL>(x, x_lds, k);
     __syncthreads();
     h2 xp[CPL][16];
@@ -74,12 +76,12 @@ gemv_read_twin_kernel(const uint8_t* __restrict__ packed, const uint16_t* __rest
     }
 
     while (p < passes) {
+        if (p + W < passes) load_pass<LPR, CPL>(B, packed, scales, mins, clamp(row_of(p + W)), k, j);
         acc ^= fold_pass<LPR, CPL>(A);
-        if (p + 2 * W < passes) load_pass<LPR, CPL>(A, packed, scales, mins, clamp(row_of(p + 2 * W)), k, j);
         p += W;
         if (p >= passes) break;
+        if (p + W < passes) load_pass<LPR, CPL>(A, packed, scales, mins, clamp(row_of(p + W)), k, j);
         acc ^= fold_pass<LPR, CPL>(B);
-        if (p + 2 * W < passes) load_pass<LPR, CPL>(B, packed, scales, mins, clamp(row_of(p + 2 * W)), k, j);
         p += W;
     }
     acc = fold_wave(acc);

@@ -30,12 +30,15 @@ namespace q4 {
 // Batch-1 kernel: the activation slice of each lane lives in registers for
 // the whole kernel (CPL <= 4), staged once per workgroup through LDS.
 // Persistent grid: every wave walks passes p, p + W, p + 2W, ... (W = waves
-// in the grid) with D (1 or 2) passes of weights in flight; the first D
-// passes are requested before the activations are staged.  With D = 1 a
-// wave requests its next pass after computing the current one: at
-// K = 3,072 that keeps ~12 MB in flight over the chip instead of ~25 MB and
-// measured 4% faster (25,088 x 3,072: 8.63 against 9.01 us); at K = 2,048,
-// 8,192 and 11,008 two passes in flight stay faster.
+// in the grid).  How many passes of weights a wave keeps in flight is the
+// schedule D (kPassAhead2, the default: two, the next one requested after a
+// pass is computed; kPassNextFirst: the next pass requested before the
+// current one is computed, so one or two in flight).  The first passes are
+// requested before the activations are staged.  Next-first keeps about half
+// the bytes in flight at the start of a call; measured (back-to-back calls,
+// same bits): 25,088 x 3,072 8.53 against 9.01 us, 3,072 x 8,192 5.53
+// against 5.61, 25,088 x 2,048 6.56 against 6.68; ragged rows at
+// K = 11,008 6.77 against 6.01 (kept at two).
 // ---------------------------------------------------------------------------
 
 template <int LPR, int CPL, bool RAGGED, int D>
@@ -64,7 +67,8 @@ gemv_reg_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__
 
     PassLoad<CPL> A, B;
     if (p < passes) load_pass<LPR, CPL, RAGGED>(A, packed, scales, mins, clamp(row_of(p)), k, j);
-    if (D == 2 && p + W < passes) load_pass<LPR, CPL, RAGGED>(B, packed, scales, mins, clamp(row_of(p + W)), k, j);
+    if (D == kPassAhead2 && p + W < passes)
+        load_pass<LPR, CPL, RAGGED>(B, packed, scales, mins, clamp(row_of(p + W)), k, j);
 
     stage_x<LPR, CPL>(x, x_lds, k);
     __syncthreads();
@@ -73,11 +77,15 @@ gemv_reg_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__
     float xs[CPL];
     lane_activations<LPR, CPL, RAGGED>(x_lds, C, j, xp, xs);
 
-    if constexpr (D == 1) {
+    if constexpr (D == kPassNextFirst) {
         while (p < passes) {
+            if (p + W < passes) load_pass<LPR, CPL, RAGGED>(B, packed, scales, mins, clamp(row_of(p + W)), k, j);
             compute_pass<LPR, CPL>(A, xp, xs, y, row_of(p), n, j);
             p += W;
-            if (p < passes) load_pass<LPR, CPL, RAGGED>(A, packed, scales, mins, clamp(row_of(p)), k, j);
+            if (p >= passes) break;
+            if (p + W < passes) load_pass<LPR, CPL, RAGGED>(A, packed, scales, mins, clamp(row_of(p + W)), k, j);
+            compute_pass<LPR, CPL>(B, xp, xs, y, row_of(p), n, j);
+            p += W;
         }
         return;
     }
@@ -357,7 +365,7 @@ int lanes_per_row(int k) {
     return 4;  // C = 4 * (K / 128) is always a multiple of 4
 }
 
-template <int LPR, int CPL, bool RAGGED, int D = 2>
+template <int LPR, int CPL, bool RAGGED, int D = kPassAhead2>
 static hipError_t launch_reg(const GemvArgs& a, const DeviceInfo& dev, hipStream_t st) {
     constexpr int RPW = 64 / LPR;
     constexpr int kThreads = kGemvThreads;
@@ -391,15 +399,16 @@ static hipError_t dispatch_reg(int lpr, int cpl, bool ragged, const GemvArgs& a,
     if (!ragged && lpr == L && cpl == P) return launch_reg<L, P, false>(a, dev, st);
 #define Q4_REG_R(L, P) \
     if (ragged && lpr == L && cpl == P) return launch_reg<L, P, true>(a, dev, st);
-    Q4_REG(64, 1) Q4_REG(64, 2) Q4_REG(64, 3) Q4_REG(64, 4)
-    Q4_REG(32, 1) Q4_REG(32, 2)
-    // K = 3,072: one pass in flight per wave (see gemv_reg_kernel)
-    if (!ragged && lpr == 32 && cpl == 3) return launch_reg<32, 3, false, 1>(a, dev, st);
+#define Q4_REG_NF(L, P) \
+    if (!ragged && lpr == L && cpl == P) return launch_reg<L, P, false, pass_schedule(L, P, false)>(a, dev, st);
+    Q4_REG(64, 1) Q4_REG(64, 2) Q4_REG(64, 3) Q4_REG_NF(64, 4)
+    Q4_REG(32, 1) Q4_REG_NF(32, 2) Q4_REG_NF(32, 3)
     Q4_REG(16, 1) Q4_REG(16, 3)
     Q4_REG(8, 1) Q4_REG(8, 3)
     Q4_REG(4, 1) Q4_REG(4, 3)
     Q4_REG_R(64, 2) Q4_REG_R(64, 3) Q4_REG_R(64, 4) Q4_REG_R(64, 5) Q4_REG_R(64, 6)
 #undef Q4_REG
+#undef Q4_REG_NF
 #undef Q4_REG_R
     return hipErrorNotSupported;
 }

@@ -16,8 +16,7 @@
 // few projections; for each "segment" (the part of the range inside one
 // projection) the workgroup stages that projection's x once in LDS, every
 // lane copies its slice into registers, and the waves run the batch-1 pass
-// loop with the batch-1 kernel's number of passes in flight (one at
-// K = 3,072, two elsewhere).
+// loop with the batch-1 kernel's pass schedule for the mapping.
 //
 // Every row goes through compute_pass<LPR, CPL> with the same lanes, chunk
 // order, group updates and butterfly as gemv_reg_kernel for its K, so every
@@ -66,7 +65,8 @@ gemv_group_kernel(const GroupTable tab) {
 
         PassLoad<CPL> A, B;
         if (p < pend) load_pass<LPR, CPL, RAGGED>(A, packed, scales, mins, clamp(row_of(p)), k, j);
-        if (D == 2 && p + NW < pend) load_pass<LPR, CPL, RAGGED>(B, packed, scales, mins, clamp(row_of(p + NW)), k, j);
+        if (D == kPassAhead2 && p + NW < pend)
+            load_pass<LPR, CPL, RAGGED>(B, packed, scales, mins, clamp(row_of(p + NW)), k, j);
 
         // Every wave has copied the previous segment's x into registers.
         if (staged) lds_barrier();
@@ -78,11 +78,15 @@ gemv_group_kernel(const GroupTable tab) {
         float xs[CPL];
         lane_activations<LPR, CPL, RAGGED>(x_lds, C, j, xp, xs);
 
-        if constexpr (D == 1) {
+        if constexpr (D == kPassNextFirst) {
             while (p < pend) {
+                if (p + NW < pend) load_pass<LPR, CPL, RAGGED>(B, packed, scales, mins, clamp(row_of(p + NW)), k, j);
                 compute_pass<LPR, CPL>(A, xp, xs, y, row_of(p), n, j);
                 p += NW;
-                if (p < pend) load_pass<LPR, CPL, RAGGED>(A, packed, scales, mins, clamp(row_of(p)), k, j);
+                if (p >= pend) break;
+                if (p + NW < pend) load_pass<LPR, CPL, RAGGED>(A, packed, scales, mins, clamp(row_of(p + NW)), k, j);
+                compute_pass<LPR, CPL>(B, xp, xs, y, row_of(p), n, j);
+                p += NW;
             }
             continue;
         }
@@ -154,10 +158,9 @@ int group_variant(int k) {
 
 static hipError_t dispatch_group(int v, const GroupTable& tab, int max_k, const DeviceInfo& dev, hipStream_t st) {
     switch (v) {
-// The passes in flight per wave follow the batch-1 GEMV's choice (one at
-// K = 3,072, two elsewhere).
+// The pass schedule follows the batch-1 GEMV's choice for the mapping.
 #define Q4_GRP(I, L, P, R) \
-    case I: return launch_group_table<L, P, R, (L == 32 && P == 3 && !R) ? 1 : 2>(tab, max_k, dev, st);
+    case I: return launch_group_table<L, P, R, pass_schedule(L, P, R)>(tab, max_k, dev, st);
         Q4_GRP(0, 64, 1, false) Q4_GRP(1, 64, 2, false) Q4_GRP(2, 64, 3, false) Q4_GRP(3, 64, 4, false)
         Q4_GRP(4, 32, 1, false) Q4_GRP(5, 32, 2, false) Q4_GRP(6, 32, 3, false) Q4_GRP(7, 16, 1, false)
         Q4_GRP(8, 16, 3, false) Q4_GRP(9, 8, 1, false) Q4_GRP(10, 8, 3, false) Q4_GRP(11, 4, 1, false)

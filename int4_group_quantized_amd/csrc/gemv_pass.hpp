@@ -11,6 +11,17 @@
 
 namespace q4 {
 
+// Schedules of the batch-1 pass loop (passes of weights a wave keeps in
+// flight): two, the next requested after a pass is computed; or next-first,
+// the next requested before the current pass is computed.  The mapping's
+// choice is shared by the batch-1 and the grouped kernels.
+constexpr int kPassAhead2 = 2;
+constexpr int kPassNextFirst = 3;
+constexpr int pass_schedule(int lpr, int cpl, bool ragged) {
+    return !ragged && ((lpr == 32 && (cpl == 2 || cpl == 3)) || (lpr == 64 && cpl == 4)) ? kPassNextFirst
+                                                                                          : kPassAhead2;
+}
+
 template <int CPL>
 struct PassLoad {
     u4 q[CPL];
