@@ -21,7 +21,8 @@
 // over the 64 lanes by a fixed butterfly and scaled by the row's fp16 scale.
 //
 // Persistent grid as in the int4 GEMV: every wave walks rows p, p + W, ...
-// with two rows of codes in flight, workgroups renumbered XCD by XCD.
+// with one or two rows of codes in flight (per chunk count, below),
+// workgroups renumbered XCD by XCD.
 #include "q4_device.hpp"
 #include "launch.hpp"
 
@@ -79,7 +80,13 @@ __device__ __forceinline__ void head_compute(const HeadRow<CPL>& R, const u4 (&x
     if (j == 0 && row < n) y[row] = v;
 }
 
-template <int CPL, bool RAGGED>
+// D = rows of codes a wave keeps in flight: 2 (the next requested two rows
+// ahead, after a row is computed) or 1 (the next requested after the
+// current row is computed).  One row measured faster at 2, 3 and 8 chunks
+// per lane (16,384 x 3,072: 9.34 against 10.22 us; 16,384 x 2,048: 7.62
+// against 7.89; 4,096 x 8,192: 9.31 against 9.74; same bits) and slower at 4
+// (8,192 x 4,096: 9.08 against 8.11), so the choice is per chunk count.
+template <int CPL, bool RAGGED, int D>
 __global__ void __launch_bounds__(kHeadThreads)
 head_int8_kernel(const int8_t* __restrict__ q, const uint16_t* __restrict__ scales,
                  const uint16_t* __restrict__ x, float* __restrict__ y, int n, int k) {
@@ -94,7 +101,7 @@ head_int8_kernel(const int8_t* __restrict__ q, const uint16_t* __restrict__ scal
 
     HeadRow<CPL> A, B;
     if (p < n) head_load<CPL, RAGGED>(A, q, scales, clamp(p), k, j);
-    if (p + W < n) head_load<CPL, RAGGED>(B, q, scales, clamp(p + W), k, j);
+    if (D == 2 && p + W < n) head_load<CPL, RAGGED>(B, q, scales, clamp(p + W), k, j);
 
     // Window w = 8 activations x0..x7 -> (x0, x2), (x1, x3), (x4, x6), (x5, x7),
     // the pair order of int8_pairs for the window's two code dwords.
@@ -121,6 +128,14 @@ head_int8_kernel(const int8_t* __restrict__ q, const uint16_t* __restrict__ scal
     uint32_t magic;
     asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
+    if constexpr (D == 1) {
+        while (p < n) {
+            head_compute<CPL>(A, xr, magic, y, (int)p, n, j);
+            p += W;
+            if (p < n) head_load<CPL, RAGGED>(A, q, scales, clamp(p), k, j);
+        }
+        return;
+    }
     while (p < n) {
         head_compute<CPL>(A, xr, magic, y, (int)p, n, j);
         if (p + 2 * W < n) head_load<CPL, RAGGED>(A, q, scales, clamp(p + 2 * W), k, j);
@@ -132,16 +147,16 @@ head_int8_kernel(const int8_t* __restrict__ q, const uint16_t* __restrict__ scal
     }
 }
 
-template <int CPL, bool RAGGED>
+template <int CPL, bool RAGGED, int D = (CPL == 2 || CPL == 3 || CPL == 8) ? 1 : 2>
 static hipError_t launch_head(const int8_t* q, const uint16_t* scales, const uint16_t* x, float* y, int n, int k,
                               const DeviceInfo& dev, hipStream_t st) {
     const size_t lds = (size_t)k * 2;
-    std::atomic<int>& cached = PerDevice<&head_int8_kernel<CPL, RAGGED>>::value[dev.device];
+    std::atomic<int>& cached = PerDevice<&head_int8_kernel<CPL, RAGGED, D>>::value[dev.device];
     int per_cu = cached.load(std::memory_order_relaxed);  // once per device
     if (per_cu == 0) {
         int nb = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &nb, reinterpret_cast<const void*>(&head_int8_kernel<CPL, RAGGED>), kHeadThreads, 8192 * 2);
+            &nb, reinterpret_cast<const void*>(&head_int8_kernel<CPL, RAGGED, D>), kHeadThreads, 8192 * 2);
         if (e != hipSuccess) return e;
         per_cu = nb > 0 ? nb : 1;
         cached.store(per_cu, std::memory_order_relaxed);
@@ -149,7 +164,7 @@ static hipError_t launch_head(const int8_t* q, const uint16_t* scales, const uin
     long grid = (long)dev.num_cu * per_cu;
     const long need = ((long)n + (kHeadThreads / 64) - 1) / (kHeadThreads / 64);
     if (grid > need) grid = need;
-    hipLaunchKernelGGL((head_int8_kernel<CPL, RAGGED>), dim3((unsigned)grid), dim3(kHeadThreads), lds, st, q,
+    hipLaunchKernelGGL((head_int8_kernel<CPL, RAGGED, D>), dim3((unsigned)grid), dim3(kHeadThreads), lds, st, q,
                        scales, x, y, n, k);
     return hipGetLastError();
 }
