@@ -60,7 +60,7 @@ struct GroupTable {
 hipError_t launch_pack(const uint8_t* codes, uint8_t* packed, int64_t n, int64_t k, hipStream_t st);
 hipError_t launch_quantize(const float* W, uint8_t* packed, uint16_t* scales, uint16_t* mins, int64_t n,
                            int64_t k, hipStream_t st);
-constexpr long kQuantizeMaxGroups = 0x7FFFFFFFL * 32L;  // grid limit of the export kernel
+constexpr long kQuantizeMaxGroups = 1L << 36;  // largest export (groups of 128 values)
 hipError_t launch_head_int8(const int8_t* q, const uint16_t* scales, const uint16_t* x, float* y, int64_t n,
                             int64_t k, const DeviceInfo& dev, hipStream_t st);
 hipError_t launch_gemv(const GemvArgs& a, const DeviceInfo& dev, hipStream_t st);
