@@ -22,9 +22,11 @@
  *   y / Y   float  [B][N]    row-major fp32 results; Y = X * W^T.
  *
  * Ownership and execution model (all entry points):
- *   - Every pointer is DEVICE memory owned by the caller.  The library never
- *     allocates, frees or keeps a pointer after returning, and needs no
- *     workspace.
+ *   - Every pointer is DEVICE memory owned by the caller (except the
+ *     grouped call's descriptor array, a host array).  The library never
+ *     allocates or frees device memory, keeps no pointer after returning,
+ *     and needs no workspace; only the grouped call uses host memory of its
+ *     own, for checking its descriptors during the call.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
  *     work; they never synchronise the host.  Buffers must stay alive until
  *     the enqueued work completes.
