@@ -127,10 +127,57 @@ __device__ __forceinline__ int cols_sum_index(int c, int b) {
     return ((c / LPR) * BT + b) * LPR + (c % LPR);
 }
 
+// Lane sums through LDS for 32 lanes per row and 8 or more columns.  The
+// butterfly of reduce_lanes costs each lane 5 vector adds (and one swizzle)
+// per column, and every lane gets every sum.  Here the lanes instead write
+// their partial sums to a per-wave LDS area, a round of CR columns at a time,
+// and each of the 2 * CR outputs of the round (2 rows x CR columns) is summed
+// by 32 / PPL lanes: PPL partials in registers, then DPP adds across those
+// lanes.  The additions pair the same partial sums as reduce_lanes<32> does
+// (lanes j and j^1, then j^2, j^4, j^8, j^16), and fp32 addition is
+// commutative, so each sum has the same bits.
+template <int LPR, int BT>
+constexpr bool cols_lds_reduce() { return LPR == 32 && BT >= 8; }
+constexpr int kColsRedFloats = 512;  // per wave: 2 rows x 8 columns x 32 lanes
+
+template <int BT>
+__device__ __forceinline__ void reduce_store_cols(const float (&y)[BT], float* red, float* __restrict__ Y,
+                                                  int row0, int n, int lane, int nb) {
+    constexpr int CR = BT % 8 == 0 ? 8 : 4;  // columns per round
+    constexpr int LPO = 64 / (2 * CR);       // lanes per output
+    constexpr int PPL = 32 / LPO;            // partial sums per lane
+    const int j = lane & 31;
+    const int rsub = lane >> 5;
+    const int o = lane / LPO;                // output (row o / CR, column o % CR) of the round
+    const int e = lane % LPO;                // its lanes: e = 0 .. LPO-1, partials j = PPL*e ..
+    const float* src = red + (o * 32 + PPL * e);
+#pragma unroll
+    for (int r = 0; r < BT / CR; ++r) {
+#pragma unroll
+        for (int c = 0; c < CR; ++c) red[(rsub * CR + c) * 32 + j] = y[CR * r + c];
+        const f4 a = *reinterpret_cast<const f4*>(src);
+        float v = (a.x + a.y) + (a.z + a.w);                                    // j^1, j^2
+        if constexpr (PPL == 8) {
+            const f4 b = *reinterpret_cast<const f4*>(src + 4);
+            v = v + ((b.x + b.y) + (b.z + b.w));                                // j^4
+            v = v + dpp_move<0xB1>(v);                                          // j^8
+            v = v + dpp_move<0x4E>(v);                                          // j^16
+        } else {
+            v = v + dpp_move<0xB1>(v);                                          // j^4
+            v = v + dpp_move<0x4E>(v);                                          // j^8
+            v = v + dpp_move<0x141>(v);                                         // j^16 (quads uniform)
+        }
+        const int col = CR * r + o % CR;
+        const int row = row0 + o / CR;
+        if (e == 0 && row < n && col < nb) Y[(size_t)col * (size_t)n + row] = v * kInvUnit;
+    }
+}
+
 template <int LPR, int CPL, int BT>
 __device__ __forceinline__ void compute_pass_cols(const PassLoad<CPL>& L, const u4* __restrict__ xq,
-                                                  const float* __restrict__ xsm, float* __restrict__ Y,
-                                                  int row, int n, int j, int nb) {
+                                                  const float* __restrict__ xsm, float* red,
+                                                  float* __restrict__ Y, int row, int n, int j, int lane,
+                                                  int nb) {
     float y[BT];
 #pragma unroll
     for (int b = 0; b < BT; ++b) y[b] = 0.0f;
@@ -168,6 +215,10 @@ __device__ __forceinline__ void compute_pass_cols(const PassLoad<CPL>& L, const 
             asm volatile("" : "+v"(y[b]));
             __builtin_amdgcn_sched_barrier(0);
         }
+    }
+    if constexpr (cols_lds_reduce<LPR, BT>()) {
+        reduce_store_cols<BT>(y, red, Y, row - (lane >> 5), n, lane, nb);
+        return;
     }
 #pragma unroll
     for (int b = 0; b < BT; ++b) {
@@ -225,6 +276,7 @@ gemm_cols_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict_
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    float* red = xsm + (size_t)BT * C + (size_t)wave * kColsRedFloats;  // lane sums (LDS reduction only)
     const int j = lane % LPR;
     const int rsub = lane / LPR;
     const long passes = ((long)n + RPW - 1) / RPW;
@@ -242,7 +294,7 @@ gemm_cols_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict_
     stage_columns<LPR, BT>(X, xq, xsm, k, nb);
 
     while (p < passes) {
-        compute_pass_cols<LPR, CPL, BT>(A, xq, xsm, Y, row_of(p), n, j, nb);
+        compute_pass_cols<LPR, CPL, BT>(A, xq, xsm, red, Y, row_of(p), n, j, lane, nb);
         p += W;
         if (p < passes) load_pass<LPR, CPL>(A, packed, scales, mins, clamp(row_of(p)), k, j);
     }
@@ -470,7 +522,9 @@ static hipError_t launch_cols(const GemvArgs& a, const uint16_t* X, float* Y, in
     constexpr int RPW = 64 / LPR;
     constexpr int kThreads = cols_threads<LPR, CPL>();
     const int C = a.k >> 5;
-    const size_t lds = (size_t)BT * 4 * C * 16 + (size_t)BT * C * 4;
+    const size_t red = cols_lds_reduce<LPR, BT>() ? (size_t)(kThreads / 64) * kColsRedFloats * 4 : 0;
+    const size_t lds = (size_t)BT * 4 * C * 16 + (size_t)BT * C * 4 + red;
+    if (lds > dev.max_lds) return hipErrorNotSupported;  // the caller falls back to the batched kernel
     // Once per device: the dynamic-LDS attribute, then the occupancy it allows.
     std::atomic<int>& cached = PerDevice<&gemm_cols_kernel<LPR, CPL, BT>>::value[dev.device];
     int per_cu = cached.load(std::memory_order_acquire);
