@@ -152,7 +152,10 @@ def test_gemv_zero_and_scaling(dev):
                                  # more passes than one round of the grid, with every column in LDS:
                                  # the batched kernel (ragged rows at K = 2,176 and, for B <= 4,
                                  # 11,008; 64 lanes of three chunks at 6,144)
-                                 (4200, 2176), (4500, 11008), (5000, 6144)])
+                                 (4200, 2176), (4500, 11008), (5000, 6144),
+                                 # the column kernel at 32 lanes of two chunks (the pages' hidden
+                                 # size) and odd row counts, whose last pass has one real row
+                                 (25088, 2048), (8301, 2048), (9001, 3072)])
 def test_small_batch_bit_identical_to_gemv(dev, n, k):
     w = synth.weights(n, k, seed=n + k)
     packed, s, m = upload(w, dev, q4)
