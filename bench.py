@@ -103,6 +103,15 @@ def time_graph(torch, stream, launch, n_launch_per_graph, steps, warmup, out=Non
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
+        # the same settle phase as the eager timing: replays for SETTLE_S first
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < SETTLE_S:
+            g.replay()
+            i += 1
+            if i % 16 == 0:
+                stream.synchronize()
+        stream.synchronize()
         start.record(stream)
         for _ in range(reps):
             g.replay()

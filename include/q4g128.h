@@ -140,7 +140,7 @@ Q4_API q4_status q4g128_gemv(const uint8_t* packed, const uint16_t* scales,
  * step as launch-bound, and advises counting launches and issuing far fewer
  * kernels per layer ("What I would tell someone starting this").  Here all
  * projections whose K has the same pass mapping are streamed by one
- * persistent launch of up to 32 projections; the projections are read from
+ * persistent launch of up to 64 projections; the projections are read from
  * `descs` (a HOST array, read during the call and not kept).
  *   descs[i]: packed, scales, mins, x, y, n, k with the layout, alignment and
  *   limits of q4g128_gemv.

@@ -43,8 +43,14 @@ gemv_group_kernel(const GroupTable tab) {
     const long a = r * total / gridDim.x;
     const long e = (r + 1) * total / gridDim.x;
 
+    // The projection holding pass a: first[i] <= a < first[i + 1] (every
+    // projection has at least one pass, so first[] is strictly increasing),
+    // found by bisection over the table in the kernel arguments.
     int i = 0;
-    while (tab.first[i + 1] <= a) ++i;
+    for (int hi = tab.count; hi - i > 1;) {
+        const int mid = (i + hi) >> 1;
+        if (tab.first[mid] <= a) i = mid; else hi = mid;
+    }
     bool staged = false;
     for (; i < tab.count && tab.first[i] < e; ++i) {
         const long f0 = tab.first[i];

@@ -64,7 +64,7 @@ def test_grouped_mixed_shapes_bit_identical(dev):
 
 
 def test_grouped_more_than_one_launch_per_variant(dev):
-    """75 projections of one mapping (three launches of at most 32), rows
+    """75 projections of one mapping (two launches of at most 64), rows
     from 1 to 700, and one shared weight set under several inputs."""
     projs, cases = [], []
     shared = None
