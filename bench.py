@@ -295,7 +295,7 @@ def _time_blocks(fn, n_rows: int, budget_s: float):
 
 
 def cpu_baseline(budget_s: float):
-    """The fp64 NumPy oracle as it stands, on the GPU machine's host, before any GPU work.
+    """The fp64 NumPy oracle as it stands, on the host of the measured GPU, before any GPU work.
 
     Legs (the oracle is a reported baseline, not a target):
       * all cores: 1,024-row blocks of the fused 25,088 x 3,072 matrix at B = 1,
