@@ -39,9 +39,21 @@ namespace q4 {
 // same bits): 25,088 x 3,072 8.53 against 9.01 us, 3,072 x 8,192 5.53
 // against 5.61, 25,088 x 2,048 6.56 against 6.68; ragged rows at
 // K = 11,008 6.77 against 6.01 (kept at two).
+//
+// XF (x first): the workgroup stages x before any wave requests weights.
+// In the default order a wave's first wait, for its x window, also waits for
+// the weights it requested before (loads complete in order), and the barrier
+// then holds the workgroup until its slowest wave's first pass has arrived.
+// When every wave walks at most two passes that start-up decides the call:
+// x first measured (same bits) 3,072 x 3,072 3.30 against 3.80 us,
+// 3,072 x 8,192 4.85 against 5.56, 2,048 x 11,008 5.13 against 6.02,
+// 4,096 x 11,008 7.08 against 8.72, 2,048 x 2,048 3.05 against 3.17.  With
+// three or more passes per wave the later first request costs more than it
+// saves (25,088 x 3,072 9.05 against 8.56 us, 16,384 x 4,096 8.19 against
+// 7.98), so the host picks XF only for grids of at most two rounds.
 // ---------------------------------------------------------------------------
 
-template <int LPR, int CPL, bool RAGGED, int D>
+template <int LPR, int CPL, bool RAGGED, int D, bool XF>
 __global__ void __launch_bounds__(kGemvThreads)
 gemv_reg_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
                 const uint16_t* __restrict__ mins, const uint16_t* __restrict__ x,
@@ -66,12 +78,17 @@ gemv_reg_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__
     auto clamp = [&](int r) { return r < n ? r : n - 1; };
 
     PassLoad<CPL> A, B;
+    if constexpr (XF) {
+        stage_x<LPR, CPL>(x, x_lds, k);
+        __syncthreads();
+    }
     if (p < passes) load_pass<LPR, CPL, RAGGED>(A, packed, scales, mins, clamp(row_of(p)), k, j);
     if (D == kPassAhead2 && p + W < passes)
         load_pass<LPR, CPL, RAGGED>(B, packed, scales, mins, clamp(row_of(p + W)), k, j);
-
-    stage_x<LPR, CPL>(x, x_lds, k);
-    __syncthreads();
+    if constexpr (!XF) {
+        stage_x<LPR, CPL>(x, x_lds, k);
+        __syncthreads();
+    }
 
     h2 xp[CPL][16];
     float xs[CPL];
@@ -416,28 +433,48 @@ int lanes_per_row(int k) {
     return 4;  // C = 4 * (K / 128) is always a multiple of 4
 }
 
+// Resident workgroups per CU of one instantiation (registers bound it; the
+// LDS footprint is at most 16 KB), queried once per device.
+template <int LPR, int CPL, bool RAGGED, int D, bool XF>
+static hipError_t reg_per_cu(const DeviceInfo& dev, int* per_cu) {
+    std::atomic<int>& cached = PerDevice<&gemv_reg_kernel<LPR, CPL, RAGGED, D, XF>>::value[dev.device];
+    int v = cached.load(std::memory_order_relaxed);
+    if (v == 0) {
+        int nb = 0;
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &nb, reinterpret_cast<const void*>(&gemv_reg_kernel<LPR, CPL, RAGGED, D, XF>), kGemvThreads, 8192 * 2);
+        if (e != hipSuccess) return e;
+        v = nb > 0 ? nb : 1;
+        cached.store(v, std::memory_order_relaxed);
+    }
+    *per_cu = v;
+    return hipSuccess;
+}
+
 template <int LPR, int CPL, bool RAGGED, int D = kPassAhead2>
 static hipError_t launch_reg(const GemvArgs& a, const DeviceInfo& dev, hipStream_t st) {
     constexpr int RPW = 64 / LPR;
     constexpr int kThreads = kGemvThreads;
+    constexpr int kWaves = kThreads / 64;
     const size_t lds = (size_t)a.k * 2;
-    // Resident workgroups per CU for this instantiation (registers bound it;
-    // the LDS footprint is at most 16 KB).  Queried once per device.
-    std::atomic<int>& cached = PerDevice<&gemv_reg_kernel<LPR, CPL, RAGGED, D>>::value[dev.device];
-    int per_cu = cached.load(std::memory_order_relaxed);
-    if (per_cu == 0) {
-        int nb = 0;
-        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &nb, reinterpret_cast<const void*>(&gemv_reg_kernel<LPR, CPL, RAGGED, D>), kThreads, 8192 * 2);
-        if (e != hipSuccess) return e;
-        per_cu = nb > 0 ? nb : 1;
-        cached.store(per_cu, std::memory_order_relaxed);
-    }
     const long passes = ((long)a.n + RPW - 1) / RPW;
+    const long need = (passes + kWaves - 1) / kWaves;
+    // x first when the grid of the x-first form walks at most two passes per wave.
+    int per_cu = 0;
+    hipError_t e = reg_per_cu<LPR, CPL, RAGGED, D, true>(dev, &per_cu);
+    if (e != hipSuccess) return e;
     long grid = (long)dev.num_cu * per_cu;
-    const long need = (passes + (kThreads / 64) - 1) / (kThreads / 64);
     if (grid > need) grid = need;
-    hipLaunchKernelGGL((gemv_reg_kernel<LPR, CPL, RAGGED, D>), dim3((unsigned)grid), dim3(kThreads), lds, st,
+    if (passes <= 2 * grid * kWaves) {
+        hipLaunchKernelGGL((gemv_reg_kernel<LPR, CPL, RAGGED, D, true>), dim3((unsigned)grid), dim3(kThreads), lds,
+                           st, a.packed, a.scales, a.mins, a.x, a.y, a.n, a.k);
+        return hipGetLastError();
+    }
+    e = reg_per_cu<LPR, CPL, RAGGED, D, false>(dev, &per_cu);
+    if (e != hipSuccess) return e;
+    grid = (long)dev.num_cu * per_cu;
+    if (grid > need) grid = need;
+    hipLaunchKernelGGL((gemv_reg_kernel<LPR, CPL, RAGGED, D, false>), dim3((unsigned)grid), dim3(kThreads), lds, st,
                        a.packed, a.scales, a.mins, a.x, a.y, a.n, a.k);
     return hipGetLastError();
 }
