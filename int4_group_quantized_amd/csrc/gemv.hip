@@ -33,8 +33,9 @@ namespace q4 {
 // in the grid).  How many passes of weights a wave keeps in flight is the
 // schedule D (kPassAhead2, the default: two, the next one requested after a
 // pass is computed; kPassNextFirst: the next pass requested before the
-// current one is computed, so one or two in flight).  The first passes are
-// requested before the activations are staged.  Next-first keeps about half
+// current one is computed, so one or two in flight).  In the default form
+// the first passes are requested before the activations are staged (XF
+// below is the other order).  Next-first keeps about half
 // the bytes in flight at the start of a call; measured (back-to-back calls,
 // same bits): 25,088 x 3,072 8.53 against 9.01 us, 3,072 x 8,192 5.53
 // against 5.61, 25,088 x 2,048 6.56 against 6.68; ragged rows at
@@ -44,13 +45,18 @@ namespace q4 {
 // In the default order a wave's first wait, for its x window, also waits for
 // the weights it requested before (loads complete in order), and the barrier
 // then holds the workgroup until its slowest wave's first pass has arrived.
-// When every wave walks at most two passes that start-up decides the call:
-// x first measured (same bits) 3,072 x 3,072 3.30 against 3.80 us,
-// 3,072 x 8,192 4.85 against 5.56, 2,048 x 11,008 5.13 against 6.02,
-// 4,096 x 11,008 7.08 against 8.72, 2,048 x 2,048 3.05 against 3.17.  With
-// three or more passes per wave the later first request costs more than it
-// saves (25,088 x 3,072 9.05 against 8.56 us, 16,384 x 4,096 8.19 against
-// 7.98), so the host picks XF only for grids of at most two rounds.
+// Measured (same bits; passes per wave in brackets), x first against the
+// default order:
+//   one workgroup per CU (K = 8,192; ragged K = 11,008), at every length:
+//     3,072 x 8,192 [1.5] 4.85 / 5.56 us, 6,144 x 8,192 [3] 6.65 / 7.49,
+//     2,048 x 11,008 [1] 5.13 / 6.02, 8,192 x 11,008 [4] 10.86 / 12.32;
+//   two passes ahead (K = 4,096), up to three: 8,192 x 4,096 [2] 5.37 /
+//     5.98, 12,288 x 4,096 [3] 6.63 / 7.10, 16,384 x 4,096 [4] 8.19 / 7.98;
+//   next-first at two workgroups per CU, up to 1.5: 3,072 x 3,072 [1] 3.30
+//     / 3.80, 12,288 x 3,072 [1.5] 5.68 / 5.96, 14,336 x 3,072 [1.75] 6.83 /
+//     6.59, 25,088 x 3,072 [3.06] 9.05 / 8.56, 16,384 x 2,048 [2] 5.52 /
+//     5.37.
+// The host picks the form from the grid (launch_reg).
 // ---------------------------------------------------------------------------
 
 template <int LPR, int CPL, bool RAGGED, int D, bool XF>
@@ -459,23 +465,23 @@ static hipError_t launch_reg(const GemvArgs& a, const DeviceInfo& dev, hipStream
     const size_t lds = (size_t)a.k * 2;
     const long passes = ((long)a.n + RPW - 1) / RPW;
     const long need = (passes + kWaves - 1) / kWaves;
-    // x first when the grid of the x-first form walks at most two passes per wave.
+    // Both forms have the same register count, hence the same grid.
     int per_cu = 0;
-    hipError_t e = reg_per_cu<LPR, CPL, RAGGED, D, true>(dev, &per_cu);
+    hipError_t e = reg_per_cu<LPR, CPL, RAGGED, D, false>(dev, &per_cu);
     if (e != hipSuccess) return e;
     long grid = (long)dev.num_cu * per_cu;
     if (grid > need) grid = need;
-    if (passes <= 2 * grid * kWaves) {
+    // x first (measured per mapping; see the kernel): with one workgroup per
+    // CU always, else up to 1.5 passes per wave, or 3 with two passes ahead.
+    const long waves = grid * kWaves;
+    const bool xf = per_cu == 1 || 2 * passes <= 3 * waves || (D == kPassAhead2 && passes <= 3 * waves);
+    if (xf) {
         hipLaunchKernelGGL((gemv_reg_kernel<LPR, CPL, RAGGED, D, true>), dim3((unsigned)grid), dim3(kThreads), lds,
                            st, a.packed, a.scales, a.mins, a.x, a.y, a.n, a.k);
-        return hipGetLastError();
+    } else {
+        hipLaunchKernelGGL((gemv_reg_kernel<LPR, CPL, RAGGED, D, false>), dim3((unsigned)grid), dim3(kThreads), lds,
+                           st, a.packed, a.scales, a.mins, a.x, a.y, a.n, a.k);
     }
-    e = reg_per_cu<LPR, CPL, RAGGED, D, false>(dev, &per_cu);
-    if (e != hipSuccess) return e;
-    grid = (long)dev.num_cu * per_cu;
-    if (grid > need) grid = need;
-    hipLaunchKernelGGL((gemv_reg_kernel<LPR, CPL, RAGGED, D, false>), dim3((unsigned)grid), dim3(kThreads), lds, st,
-                       a.packed, a.scales, a.mins, a.x, a.y, a.n, a.k);
     return hipGetLastError();
 }
 
