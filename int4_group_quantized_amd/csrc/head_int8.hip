@@ -86,7 +86,11 @@ __device__ __forceinline__ void head_compute(const HeadRow<CPL>& R, const u4 (&x
 // per lane (16,384 x 3,072: 9.34 against 10.22 us; 16,384 x 2,048: 7.62
 // against 7.89; 4,096 x 8,192: 9.31 against 9.74; same bits) and slower at 4
 // (8,192 x 4,096: 9.08 against 8.11), so the choice is per chunk count.
-template <int CPL, bool RAGGED, int D>
+// XF: x is staged before the first rows are requested (otherwise after), so
+// that the staging's wait does not also wait for those rows (loads complete
+// in order) and the barrier does not hold the workgroup for its slowest
+// wave's rows; the host picks it for short grids (launch_head).
+template <int CPL, bool RAGGED, int D, bool XF>
 __global__ void __launch_bounds__(kHeadThreads)
 head_int8_kernel(const int8_t* __restrict__ q, const uint16_t* __restrict__ scales,
                  const uint16_t* __restrict__ x, float* __restrict__ y, int n, int k) {
@@ -100,8 +104,10 @@ head_int8_kernel(const int8_t* __restrict__ q, const uint16_t* __restrict__ scal
     auto clamp = [&](long r) { return (int)(r < n ? r : n - 1); };
 
     HeadRow<CPL> A, B;
-    if (p < n) head_load<CPL, RAGGED>(A, q, scales, clamp(p), k, j);
-    if (D == 2 && p + W < n) head_load<CPL, RAGGED>(B, q, scales, clamp(p + W), k, j);
+    if constexpr (!XF) {
+        if (p < n) head_load<CPL, RAGGED>(A, q, scales, clamp(p), k, j);
+        if (D == 2 && p + W < n) head_load<CPL, RAGGED>(B, q, scales, clamp(p + W), k, j);
+    }
 
     // Window w = 8 activations x0..x7 -> (x0, x2), (x1, x3), (x4, x6), (x5, x7),
     // the pair order of int8_pairs for the window's two code dwords.
@@ -112,6 +118,10 @@ head_int8_kernel(const int8_t* __restrict__ q, const uint16_t* __restrict__ scal
                      __builtin_amdgcn_perm(v.w, v.z, 0x05040100u), __builtin_amdgcn_perm(v.w, v.z, 0x07060302u)};
     }
     __syncthreads();
+    if constexpr (XF) {
+        if (p < n) head_load<CPL, RAGGED>(A, q, scales, clamp(p), k, j);
+        if (D == 2 && p + W < n) head_load<CPL, RAGGED>(B, q, scales, clamp(p + W), k, j);
+    }
     u4 xr[CPL][2];
 #pragma unroll
     for (int t = 0; t < CPL; ++t) {
@@ -151,12 +161,12 @@ template <int CPL, bool RAGGED, int D = (CPL == 2 || CPL == 3 || CPL == 8) ? 1 :
 static hipError_t launch_head(const int8_t* q, const uint16_t* scales, const uint16_t* x, float* y, int n, int k,
                               const DeviceInfo& dev, hipStream_t st) {
     const size_t lds = (size_t)k * 2;
-    std::atomic<int>& cached = PerDevice<&head_int8_kernel<CPL, RAGGED, D>>::value[dev.device];
-    int per_cu = cached.load(std::memory_order_relaxed);  // once per device
+    std::atomic<int>& cached = PerDevice<&head_int8_kernel<CPL, RAGGED, D, false>>::value[dev.device];
+    int per_cu = cached.load(std::memory_order_relaxed);  // once per device; both forms have the same registers
     if (per_cu == 0) {
         int nb = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &nb, reinterpret_cast<const void*>(&head_int8_kernel<CPL, RAGGED, D>), kHeadThreads, 8192 * 2);
+            &nb, reinterpret_cast<const void*>(&head_int8_kernel<CPL, RAGGED, D, false>), kHeadThreads, 8192 * 2);
         if (e != hipSuccess) return e;
         per_cu = nb > 0 ? nb : 1;
         cached.store(per_cu, std::memory_order_relaxed);
@@ -164,8 +174,19 @@ static hipError_t launch_head(const int8_t* q, const uint16_t* scales, const uin
     long grid = (long)dev.num_cu * per_cu;
     const long need = ((long)n + (kHeadThreads / 64) - 1) / (kHeadThreads / 64);
     if (grid > need) grid = need;
-    hipLaunchKernelGGL((head_int8_kernel<CPL, RAGGED, D>), dim3((unsigned)grid), dim3(kHeadThreads), lds, st, q,
-                       scales, x, y, n, k);
+    // x staged before the first row is requested when every wave has one row,
+    // or two with two rows ahead (as for the int4 GEMV; measured, same bits:
+    // 4,096 x 8,192 7.67 against 9.29 us, 4,096 x 3,072 4.21 against 4.62,
+    // 8,192 x 4,096 7.58 against 8.17; 16,384 x 3,072, two rows per wave with
+    // one ahead, 9.58 against 9.37, keeps the default order).
+    const long waves = grid * (kHeadThreads / 64);
+    if ((long)n <= waves || (D == 2 && (long)n <= 2 * waves)) {
+        hipLaunchKernelGGL((head_int8_kernel<CPL, RAGGED, D, true>), dim3((unsigned)grid), dim3(kHeadThreads), lds,
+                           st, q, scales, x, y, n, k);
+    } else {
+        hipLaunchKernelGGL((head_int8_kernel<CPL, RAGGED, D, false>), dim3((unsigned)grid), dim3(kHeadThreads), lds,
+                           st, q, scales, x, y, n, k);
+    }
     return hipGetLastError();
 }
 
