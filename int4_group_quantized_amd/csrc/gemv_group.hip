@@ -27,7 +27,7 @@
 
 namespace q4 {
 
-template <int LPR, int CPL, bool RAGGED, int D>
+template <int LPR, int CPL, bool RAGGED, int D, bool XF>
 __global__ void __launch_bounds__(kGemvThreads)
 gemv_group_kernel(const GroupTable tab) {
     constexpr int RPW = 64 / LPR;
@@ -69,16 +69,25 @@ gemv_group_kernel(const GroupTable tab) {
         auto row_of = [&](long pp) { return (int)(pp * RPW) + rsub; };
         auto clamp = [&](int rr) { return rr < n ? rr : n - 1; };
 
+        // XF: x is staged before the segment's first weights are requested
+        // (as the batch-1 kernel does for short grids), else after.
         PassLoad<CPL> A, B;
-        if (p < pend) load_pass<LPR, CPL, RAGGED>(A, packed, scales, mins, clamp(row_of(p)), k, j);
-        if (D == kPassAhead2 && p + NW < pend)
-            load_pass<LPR, CPL, RAGGED>(B, packed, scales, mins, clamp(row_of(p + NW)), k, j);
+        if constexpr (!XF) {
+            if (p < pend) load_pass<LPR, CPL, RAGGED>(A, packed, scales, mins, clamp(row_of(p)), k, j);
+            if (D == kPassAhead2 && p + NW < pend)
+                load_pass<LPR, CPL, RAGGED>(B, packed, scales, mins, clamp(row_of(p + NW)), k, j);
+        }
 
         // Every wave has copied the previous segment's x into registers.
         if (staged) lds_barrier();
         stage_x<LPR, CPL>(tab.x[i], x_lds, k);
         __syncthreads();
         staged = true;
+        if constexpr (XF) {
+            if (p < pend) load_pass<LPR, CPL, RAGGED>(A, packed, scales, mins, clamp(row_of(p)), k, j);
+            if (D == kPassAhead2 && p + NW < pend)
+                load_pass<LPR, CPL, RAGGED>(B, packed, scales, mins, clamp(row_of(p + NW)), k, j);
+        }
 
         h2 xp[CPL][16];
         float xs[CPL];
@@ -118,13 +127,14 @@ template <int LPR, int CPL, bool RAGGED, int D>
 static hipError_t launch_group_table(const GroupTable& tab, int max_k, const DeviceInfo& dev, hipStream_t st) {
     constexpr int kThreads = kGemvThreads;
     const size_t lds = (size_t)max_k * 2;
-    std::atomic<int>& cached = PerDevice<&gemv_group_kernel<LPR, CPL, RAGGED, D>>::value[dev.device];
+    // Both forms have the same registers, hence the same occupancy.
+    std::atomic<int>& cached = PerDevice<&gemv_group_kernel<LPR, CPL, RAGGED, D, false>>::value[dev.device];
     int per_cu = cached.load(std::memory_order_relaxed);
     if (per_cu == 0) {
         int nb = 0;
         // The largest x this instantiation stages: K = 32 * LPR * CPL.
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &nb, reinterpret_cast<const void*>(&gemv_group_kernel<LPR, CPL, RAGGED, D>), kThreads,
+            &nb, reinterpret_cast<const void*>(&gemv_group_kernel<LPR, CPL, RAGGED, D, false>), kThreads,
             (size_t)64 * LPR * CPL);
         if (e != hipSuccess) return e;
         per_cu = nb > 0 ? nb : 1;
@@ -134,7 +144,16 @@ static hipError_t launch_group_table(const GroupTable& tab, int max_k, const Dev
     long grid = (long)dev.num_cu * per_cu;
     const long need = (total + (kThreads / 64) - 1) / (kThreads / 64);
     if (grid > need) grid = need;
-    hipLaunchKernelGGL((gemv_group_kernel<LPR, CPL, RAGGED, D>), dim3((unsigned)grid), dim3(kThreads), lds, st, tab);
+    // x first with one workgroup per CU (measured on the pages' step, whose
+    // K = 11,008 projections run at one workgroup per CU: 238.2-238.6 against
+    // 241.0-241.3 us, same bits; the 36-layer step's K = 8,192 launch, also
+    // one per CU, is unchanged; at two per CU it is not faster either).
+    if (per_cu == 1)
+        hipLaunchKernelGGL((gemv_group_kernel<LPR, CPL, RAGGED, D, true>), dim3((unsigned)grid), dim3(kThreads), lds,
+                           st, tab);
+    else
+        hipLaunchKernelGGL((gemv_group_kernel<LPR, CPL, RAGGED, D, false>), dim3((unsigned)grid), dim3(kThreads), lds,
+                           st, tab);
     return hipGetLastError();
 }
 
