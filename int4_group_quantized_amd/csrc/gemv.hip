@@ -286,7 +286,7 @@ __device__ __forceinline__ void stage_columns(const uint16_t* __restrict__ X, u4
 template <int LPR, int CPL>
 constexpr int cols_threads() { return (LPR <= 32 && CPL <= 3) ? 1024 : 512; }
 
-template <int LPR, int CPL, int BT>
+template <int LPR, int CPL, int BT, bool XF>
 __global__ void __launch_bounds__((cols_threads<LPR, CPL>()))
 gemm_cols_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
                  const uint16_t* __restrict__ mins, const uint16_t* __restrict__ X,
@@ -311,10 +311,21 @@ gemm_cols_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict_
     // One pass of weights in flight per wave: the next pass is requested after
     // the current one is computed.  Against two passes ahead this measured
     // 5-7% faster at B = 2 and 4, 1-3% at B = 8 to 16 (25,088 x 3,072 and
-    // 25,088 x 2,048, same bits).
+    // 25,088 x 2,048, same bits); the next pass requested before the current
+    // one is computed measured 5-12% slower.  XF: the columns are staged
+    // before the first pass is requested, chosen with one workgroup per CU
+    // and at most 4 column slots.  Measured on two boxes (same bits), x first
+    // against the default order: 25,088 x 3,072 at B = 2 2.5% and 4.8%
+    // faster, B = 4 2.0% and 1.6%; 25,088 x 2,048 at B = 4 3.4% and 5.4%;
+    // but at B = 8 and 16 from 4.9% faster to 4.4% slower, box by box.
     PassLoad<CPL> A;
-    if (p < passes) load_pass<LPR, CPL>(A, packed, scales, mins, clamp(row_of(p)), k, j);
+    if constexpr (!XF) {
+        if (p < passes) load_pass<LPR, CPL>(A, packed, scales, mins, clamp(row_of(p)), k, j);
+    }
     stage_columns<LPR, BT>(X, xq, xsm, k, nb);
+    if constexpr (XF) {
+        if (p < passes) load_pass<LPR, CPL>(A, packed, scales, mins, clamp(row_of(p)), k, j);
+    }
 
     while (p < passes) {
         compute_pass_cols<LPR, CPL, BT>(A, xq, xsm, red, Y, row_of(p), n, j, lane, nb);
@@ -568,12 +579,16 @@ static hipError_t launch_cols(const GemvArgs& a, const uint16_t* X, float* Y, in
     const size_t red = cols_lds_reduce<LPR, BT>() ? (size_t)(kThreads / 64) * kColsRedFloats * 4 : 0;
     const size_t lds = (size_t)BT * 4 * C * 16 + (size_t)BT * C * 4 + red;
     if (lds > dev.max_lds) return hipErrorNotSupported;  // the caller falls back to the batched kernel
-    // Once per device: the dynamic-LDS attribute, then the occupancy it allows.
-    std::atomic<int>& cached = PerDevice<&gemm_cols_kernel<LPR, CPL, BT>>::value[dev.device];
+    // Once per device: the dynamic-LDS attribute of both forms, then the
+    // occupancy (the same for both: same registers).
+    std::atomic<int>& cached = PerDevice<&gemm_cols_kernel<LPR, CPL, BT, false>>::value[dev.device];
     int per_cu = cached.load(std::memory_order_acquire);
     if (per_cu == 0) {
-        const void* fn = reinterpret_cast<const void*>(&gemm_cols_kernel<LPR, CPL, BT>);
+        const void* fn = reinterpret_cast<const void*>(&gemm_cols_kernel<LPR, CPL, BT, false>);
+        const void* fx = reinterpret_cast<const void*>(&gemm_cols_kernel<LPR, CPL, BT, true>);
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dev.max_lds);
+        if (e != hipSuccess) return e;
+        e = hipFuncSetAttribute(fx, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dev.max_lds);
         if (e != hipSuccess) return e;
         int nb_cu = 0;
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb_cu, fn, kThreads, lds);
@@ -585,8 +600,12 @@ static hipError_t launch_cols(const GemvArgs& a, const uint16_t* X, float* Y, in
     long grid = (long)dev.num_cu * per_cu;
     const long need = (passes + (kThreads / 64) - 1) / (kThreads / 64);
     if (grid > need) grid = need;
-    hipLaunchKernelGGL((gemm_cols_kernel<LPR, CPL, BT>), dim3((unsigned)grid), dim3(kThreads), lds, st,
-                       a.packed, a.scales, a.mins, X, Y, a.n, a.k, nb);
+    if (per_cu == 1 && BT <= 4)
+        hipLaunchKernelGGL((gemm_cols_kernel<LPR, CPL, BT, true>), dim3((unsigned)grid), dim3(kThreads), lds, st,
+                           a.packed, a.scales, a.mins, X, Y, a.n, a.k, nb);
+    else
+        hipLaunchKernelGGL((gemm_cols_kernel<LPR, CPL, BT, false>), dim3((unsigned)grid), dim3(kThreads), lds, st,
+                           a.packed, a.scales, a.mins, X, Y, a.n, a.k, nb);
     return hipGetLastError();
 }
 
