@@ -88,3 +88,14 @@ def test_head_int8_row_permutation(dev):
     y = run(q, s, x, dev)
     yp = run(np.ascontiguousarray(q[perm]), np.ascontiguousarray(s[perm]), x, dev)
     assert np.array_equal(yp, y[perm])
+
+
+@pytest.mark.parametrize("n_tall,n_short,k", [(16384, 4096, 3072), (8192, 2048, 4096)])
+def test_head_int8_rows_do_not_depend_on_height(dev, n_tall, n_short, k):
+    """The first n_short rows of a tall head matrix, given as a matrix of their
+    own, give the same bits: the short matrix stages x before its first rows
+    are requested (one row per wave), the tall 16,384 x 3,072 one after."""
+    q, s, x = synth.head_int8_case(n_tall, k, seed=n_tall + k)
+    y_tall = run(q, s, x, dev)
+    y_short = run(q[:n_short].copy(), s[:n_short].copy(), x, dev)
+    assert np.array_equal(y_short.view(np.uint32), y_tall[:n_short].view(np.uint32))

@@ -221,6 +221,26 @@ def test_determinism_and_row_permutation(dev):
     assert np.array_equal(cpu(q4.q4g128_gemv(pp, sp, mp, xd)), y0[perm])
 
 
+@pytest.mark.parametrize("n_tall,n_short,k", [(25088, 3072, 3072), (25088, 2048, 2048), (16384, 4096, 4096),
+                                               (6144, 2048, 8192), (8192, 2048, 11008)])
+def test_gemv_rows_do_not_depend_on_height(dev, n_tall, n_short, k):
+    """A row's result does not depend on the matrix it sits in: the first
+    n_short rows of a tall matrix, given as a matrix of their own, give the
+    same bits.  The short matrices run x-first (every wave has at most one or
+    two passes, or the mapping runs one workgroup per CU) and the tall ones at
+    K = 2,048 to 4,096 the default order, so this also holds the two launch
+    orders of the batch-1 kernel to the same bits."""
+    w = synth.weights(n_tall, k, seed=n_tall + k)
+    x = synth.activations(1, k, seed=9)[0]
+    xd = to_dev_f16(x, dev)
+    packed, s, m = upload(w, dev, q4)
+    y_tall = cpu(q4.q4g128_gemv(packed, s, m, xd))
+    short = synth.Weights(w.codes[:n_short].copy(), w.scales[:n_short].copy(), w.mins[:n_short].copy())
+    ps, ss, ms = upload(short, dev, q4)
+    y_short = cpu(q4.q4g128_gemv(ps, ss, ms, xd))
+    assert np.array_equal(y_short.view(np.uint32), y_tall[:n_short].view(np.uint32))
+
+
 def test_non_default_stream(dev):
     w, x = synth.gemv_case(512, 1024, seed=5)
     packed, s, m = upload(w, dev, q4)
