@@ -17,8 +17,9 @@
 //    read both operands from registers, with no LDS tile and no barrier per
 //    group;
 //  * each weight byte of the slice is read and dequantised by exactly one
-//    wave; a lane (r = lane & 15, q = lane >> 4) holds chunk q (32 codes) of
-//    row r of a tile, requested two tiles ahead;
+//    wave; at the matrix instructions a lane (r = lane & 15, q = lane >> 4)
+//    holds chunk q (32 codes) of row r of a tile; the next tile is requested
+//    when a tile starts;
 //  * after each tile the waves' partial sums meet in LDS (double-buffered by
 //    tile parity, one barrier per tile) and wave t adds the NW partials of
 //    token tile t in wave order, a fixed order, into the tile's total in LDS
@@ -26,6 +27,27 @@
 //    end.
 // Groups past K get zero scale and minimum (their weights are +0); rows and
 // tokens past the ends are clamped copies whose results are not stored.
+//
+// Load patterns.  Requested in the matrix-core layout, one 16-byte-per-lane
+// load touches 16 rows (or tokens) at 64 bytes each.  Instead consecutive
+// lanes request consecutive 16-byte words of a row, and each wave hands the
+// words to the matrix-core layout through an LDS block of its own (one
+// write and one read per word; padded rows, so the reads are conflict-free):
+//  * activations, once per round: the 16 tokens x 16 words of a (group,
+//    token tile) per four loads;
+//  * codes, per tile, with one or two token tiles: the wave's 16 rows x 4*GR
+//    words (with three, the registers this takes would spill, and the codes
+//    keep the matrix-core layout);
+//  * scales and minimums, per tile: one 2-byte load each by lane
+//    row * GR + group, handed out with ds_bpermute.
+// Measured on the fused matrix (same bits, fp16-weight form), all three and
+// one tile ahead against the matrix-core layout two tiles ahead: M = 1 14.48
+// -> 12.05 us, 16: 16.94 -> 13.22, 32: 20.97 -> 16.80; with three token
+// tiles (activations, scales and minimums only) M = 34 22.09 -> 18.16, 48:
+// 24.93 -> 19.76.  Two tiles ahead with the new patterns: 1 to 6% slower
+// with one or two token tiles; with three the codes' pattern then spills
+// (M = 34 26.1 us).  A twin of the loads alone (no arithmetic) gave the
+// activations 3.8 against 7.4 us and the codes 10.2 against 12.0 us.
 //
 // v_mfma_f32_16x16x32_f16 step s (0..3) contracts dword s of every lane's
 // chunk: B = the lane's 8 fp16 weights (EPI: the 8 exact codes as fp16
@@ -44,6 +66,7 @@ namespace q4 {
 
 constexpr int kSplitWaves = 8;
 constexpr int kSplitMaxTiles = 8;  // 16-row tiles per workgroup (128 rows)
+constexpr int kSplitStageWords = 16 * 17;  // 16-byte words of a wave's staging block
 
 template <int TT, int GR, int NW, bool EPI>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
@@ -54,10 +77,14 @@ prefill_split_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restr
     f4* part = lds_f4;                         // [2][NW][TT][64] partial sums per tile parity
     f4* tot = lds_f4 + 2 * NW * TT * 64;       // [kSplitMaxTiles][TT][64] totals of the slice
     constexpr int PER_ROUND = NW * GR;
+    constexpr int W = 4 * GR;                  // words of a row in the wave's part of a tile
+    constexpr bool kRowCodes = TT <= 2;        // codes requested in row order
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // The wave's staging block: 16 rows of up to 16 words, padded to 17.
+    u4* stg = reinterpret_cast<u4*>(tot + kSplitMaxTiles * TT * 64) + wave * kSplitStageWords;
     const int r = lane & 15;
     const int q = lane >> 4;
     const int G = k >> 7;
@@ -71,60 +98,82 @@ prefill_split_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restr
     for (int rd = 0; rd < R; ++rd) {
         const int gw = rd * PER_ROUND + wave * GR;  // first group of this wave (uniform)
 
-        // Weight ring: slot [tile parity][group of the wave].
-        u4 wq[2][GR];
-        uint16_t ws[2][GR], wm[2][GR];
-        auto load_w = [&](int p, int gi, int rt) {
-            int row = row_lo + 16 * rt + r;
+        // The tile in flight: codes (word gi*64 + lane of the tile's 16 x W
+        // in row order, or chunk q of row r of group gi), and the scale and
+        // minimum of (row lane / GR, group lane % GR).
+        u4 wq[GR];
+        uint16_t ws, wm;
+        auto load_codes = [&](int gi, int rt) {
+            int row, g, c;
+            if constexpr (kRowCodes) {
+                const int w = gi * 64 + lane;
+                row = w / W;
+                g = gw + (w % W) / 4;
+                c = w & 3;
+            } else {
+                row = r;
+                g = gw + gi;
+                c = q;
+            }
+            row = row_lo + 16 * rt + row;
             row = row < row_hi ? row : row_hi - 1;
-            int g = gw + gi;
             g = g < G ? g : G - 1;
-            wq[p][gi] = __builtin_nontemporal_load(
-                reinterpret_cast<const u4*>(packed + (size_t)row * row_bytes) + g * 4 + q);
-            ws[p][gi] = scales[(size_t)row * G + g];
-            wm[p][gi] = mins[(size_t)row * G + g];
+            wq[gi] = __builtin_nontemporal_load(
+                reinterpret_cast<const u4*>(packed + (size_t)row * row_bytes) + g * 4 + c);
+        };
+        auto load_sm = [&](int rt) {
+            const int l2 = lane < 16 * GR ? lane : 0;
+            int row = row_lo + 16 * rt + l2 / GR;
+            row = row < row_hi ? row : row_hi - 1;
+            int g = gw + l2 % GR;
+            g = g < G ? g : G - 1;
+            ws = scales[(size_t)row * G + g];
+            wm = mins[(size_t)row * G + g];
+        };
+        auto load_w = [&](int rt) {
+#pragma unroll
+            for (int gi = 0; gi < GR; ++gi) load_codes(gi, rt);
+            load_sm(rt);
         };
         // With one or three token tiles the activations are requested before
-        // the first two tiles' weights (loads complete in order, so staging
-        // them then waits for them alone); measured on the fused matrix (same
-        // bits): M = 34 21.31 against 21.87 us, epilogue form 23.12 against
-        // 24.10; M = 1 to 16 0.7-2.6% faster; but with two tiles (M = 24, 32)
-        // 1.0-2.5% slower, so those keep the weights first.
+        // the first tile's weights (loads complete in order, so staging them
+        // then waits for them alone); with two, after (measured 1.0-2.5%
+        // faster with the earlier patterns at M = 24 and 32).
         constexpr bool kActFirst = TT != 2;
-        if constexpr (!kActFirst) {
-#pragma unroll
-            for (int p = 0; p < 2; ++p)
-#pragma unroll
-                for (int gi = 0; gi < GR; ++gi) load_w(p, gi, p);
-        }
+        if constexpr (!kActFirst) load_w(0);
 
         // Activation fragments of this wave's groups: [group][k-step][token tile].
+        // Requested as word s*64 + lane of the (group, token tile)'s 16 tokens
+        // x 16 words, then moved to lane (r, q): words 4q + s of token r.
         u4 xa[GR][4][TT];
 #pragma unroll
         for (int gi = 0; gi < GR; ++gi) {
             int g = gw + gi;
             g = g < G ? g : G - 1;
 #pragma unroll
+            for (int t = 0; t < TT; ++t)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int w = s * 64 + lane;
+                    int tok = 16 * t + (w >> 4);
+                    tok = tok < m ? tok : m - 1;
+                    xa[gi][s][t] = reinterpret_cast<const u4*>(X + (size_t)tok * (size_t)k + (size_t)g * 128)[w & 15];
+                }
+        }
+#pragma unroll
+        for (int gi = 0; gi < GR; ++gi)
+#pragma unroll
             for (int t = 0; t < TT; ++t) {
-                int tok = 16 * t + r;
-                tok = tok < m ? tok : m - 1;
-                const u4* xp = reinterpret_cast<const u4*>(X + (size_t)tok * (size_t)k + (size_t)g * 128 + 32 * q);
 #pragma unroll
-                for (int s = 0; s < 4; ++s) xa[gi][s][t] = kActFirst ? xp[s] : permute_window(xp[s]);
+                for (int s = 0; s < 4; ++s) {
+                    const int w = s * 64 + lane;
+                    stg[(w >> 4) * 17 + (w & 15)] = xa[gi][s][t];
+                }
+#pragma unroll
+                for (int s = 0; s < 4; ++s) xa[gi][s][t] = permute_window(stg[r * 17 + 4 * q + s]);
             }
-        }
-        if constexpr (kActFirst) {
-#pragma unroll
-            for (int p = 0; p < 2; ++p)
-#pragma unroll
-                for (int gi = 0; gi < GR; ++gi) load_w(p, gi, p);
-#pragma unroll
-            for (int gi = 0; gi < GR; ++gi)
-#pragma unroll
-                for (int t = 0; t < TT; ++t)
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) xa[gi][s][t] = permute_window(xa[gi][s][t]);
-        }
+        if constexpr (kActFirst) load_w(0);
+
         // EPI: the A operand of the minimum term, S_g of token r of each
         // token tile for the wave's group q (zero for q >= GR): the lane's 32
         // columns of token r, then the other three k-slots of the token
@@ -158,17 +207,39 @@ prefill_split_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restr
             f4 acc[TT];
 #pragma unroll
             for (int t = 0; t < TT; ++t) acc[t] = zero;
+            // Take the tile's codes (in row order: all, through the staging
+            // block; otherwise each group's when it is used), scales and
+            // minimums out of the registers, requesting the next tile's in
+            // their place.
+            if constexpr (kRowCodes) {
+#pragma unroll
+                for (int gi = 0; gi < GR; ++gi) {
+                    const int w = gi * 64 + lane;
+                    stg[(w / W) * (W + 1) + w % W] = wq[gi];
+                    load_codes(gi, rt + 1);
+                }
+            }
+            const uint32_t sm = (uint32_t)ws | ((uint32_t)wm << 16);
+            load_sm(rt + 1);
             float bm = 0.0f;  // EPI: min of this lane's row for the wave's group q
 #pragma unroll
             for (int gi = 0; gi < GR; ++gi) {
                 const uint32_t keep = (uint32_t)__builtin_amdgcn_readfirstlane(-(int)(gw + gi < G));
+                const uint32_t smg = (uint32_t)__builtin_amdgcn_ds_bpermute((r * GR + gi) * 4, (int)sm) & keep;
+                const uint16_t sb = (uint16_t)smg;
+                const uint16_t mb = (uint16_t)(smg >> 16);
+                u4 cw;
+                if constexpr (kRowCodes) {
+                    cw = stg[r * (W + 1) + 4 * gi + q];
+                } else {
+                    cw = wq[gi];
+                    load_codes(gi, rt + 1);
+                }
                 if constexpr (EPI) {
                     // Exact codes as fp16 denormals c * 2^-20 (each nibble moved
                     // to mantissa bits 4..7), in the pair order of dequant_dword.
-                    const float sf = f16_bits_to_f32((uint16_t)(ws[p][gi] & keep)) * kInvUnit;
-                    bm = q == gi ? f16_bits_to_f32((uint16_t)(wm[p][gi] & keep)) : bm;
-                    const u4 cw = wq[p][gi];
-                    load_w(p, gi, rt + 2);
+                    const float sf = f16_bits_to_f32(sb) * kInvUnit;
+                    bm = q == gi ? f16_bits_to_f32(mb) : bm;
                     f4 cg[TT];
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
@@ -187,8 +258,7 @@ prefill_split_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restr
                         for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(sf, cg[t][i], acc[t][i]);
                 } else {
                     uint32_t wv[16];
-                    weights_fp16(wq[p][gi], (uint16_t)(ws[p][gi] & keep), (uint16_t)(wm[p][gi] & keep), kc, wv);
-                    load_w(p, gi, rt + 2);
+                    weights_fp16(cw, sb, mb, kc, wv);
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
                         const u4 bw = {wv[4 * s + 0], wv[4 * s + 1], wv[4 * s + 2], wv[4 * s + 3]};
@@ -247,8 +317,8 @@ template <int TT, int GR, bool EPI>
 static hipError_t launch_split(const GemvArgs& a, const uint16_t* X, float* Y, int m,
                                const DeviceInfo& dev, hipStream_t st) {
     constexpr int NW = kSplitWaves;
-    const size_t lds = ((size_t)2 * NW * TT + (size_t)kSplitMaxTiles * TT) * 64 *
-                       sizeof(f4);
+    const size_t lds = ((size_t)2 * NW * TT + (size_t)kSplitMaxTiles * TT) * 64 * sizeof(f4) +
+                       (size_t)NW * kSplitStageWords * sizeof(u4);
     std::atomic<int>& attr_set = PerDevice<&prefill_split_kernel<TT, GR, NW, EPI>>::value[dev.device];
     if (attr_set.load(std::memory_order_acquire) == 0) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_split_kernel<TT, GR, NW, EPI>),
