@@ -8,7 +8,8 @@
 //
 // What bounds this shape is not the matrix cores but the activations: every
 // workgroup that covers all of K for its rows reads all of its tokens' X
-// from L2, and the L2 delivers about 10 TB/s to the CUs in aggregate.  So a
+// from L2 (about 10 TB/s in aggregate measured with loads in the matrix-core
+// operand layout).  So a
 // workgroup takes a block of 128 tokens and twice the rows of the
 // one-block-per-CU cut: the blocks of one row slice are placed on one XCD
 // (workgroups are dealt to the 8 XCDs round-robin), where the second read
