@@ -19,7 +19,8 @@
 // 16 row tiles of 16, 8 in the EPI form; tokens [tb*128, tb*128 + 128)):
 //  * wave w owns row tiles w and w + 8 (EPI: row tile w) for all 8 token
 //    tiles of the block: 16 accumulator tiles, 64 VGPRs;
-//  * it streams its tiles' packed codes, scales and mins four groups ahead
+//  * it streams its tiles' packed codes, scales and mins a window of four
+//    groups ahead (RC, below) or four groups ahead in the operand layout,
 //    and dequantises one dword (8 weights) per tile and k-step in registers,
 //    w = fma(code, scale, min) rounded once to fp16;
 //  * the activations of one 128-column group sit in a double-buffered LDS
@@ -65,7 +66,7 @@ constexpr int kPairDX = 2;        // activation groups in flight
 // wave of its SIMD has two (the busiest SIMD sets the time) and is
 // cheaper than a branch inside the group loop (measured: the epilogue form
 // then spills).
-template <bool EPI, int RW>
+template <bool EPI, int RW, bool RC>
 __global__ void __launch_bounds__(64 * kPairWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
                     const uint16_t* __restrict__ mins, const uint16_t* __restrict__ X,
@@ -77,6 +78,18 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
     static_assert(RW == 1 || RW == 2, "row tiles per wave");
     __shared__ u4 xs[2][TB][4][64];
     constexpr bool kRowAct = !EPI || RW == 2;
+    // RC: each wave's codes of a window of U groups requested in row order
+    // (16 rows x 16 words per row tile, four rows x 256 B per load) and moved
+    // to the operand layout through this staging block (rows padded to 17
+    // words); the window's scales and minimums one 2-byte load each per row
+    // tile, by lane row * U + group, handed out with ds_bpermute.  The next
+    // window is requested when a window starts.  Measured against the
+    // operand layout four groups ahead (same bits, fused matrix): fp16
+    // weights M = 193 59.0 -> 53.1 us, 256 59.0 -> 54.6, 512 113.1 -> 109.7;
+    // epilogue form with one row tile per wave (65 to 128 tokens) 1-6%
+    // faster, with two 1-4% slower (M = 256 1.1% faster), so that one keeps
+    // the operand layout.
+    __shared__ u4 cstage[RC ? kPairWaves * RW * 16 * 17 : 1];
     __shared__ float xsum[8][TB][16];  // EPI: S_g of every token of the block, groups g mod 8
 
     const int tid = threadIdx.x;
@@ -126,6 +139,33 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
     // Fragment slot of lane l = r + 16q at k-step s (kRowAct): r XOR (4q + s).
     auto slot_of = [](int l, int s) { return kRowAct ? (l & 48) | ((l & 15) ^ ((4 * (l >> 4) + s) & 15)) : l; };
     const DequantConsts kc = make_dequant_consts();
+
+    u4* cst = cstage + (RC ? wave * RW * 16 * 17 : 0);
+    u4 wr[RW][4];          // RC: the next window's codes, word 64 i + lane of a row tile's 16 x 16
+    uint16_t wsr[RW], wmr[RW];  // RC: the next window's scale and minimum of (row lane / U, group lane % U)
+    auto load_window = [&](int g0) {
+#pragma unroll
+        for (int j = 0; j < RW; ++j) {
+            const int rb = row_lo + 16 * (wave + kPairWaves * j);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int w = 64 * i + lane;
+                int row = rb + (w >> 4);
+                row = row < row_hi ? row : row_hi - 1;
+                int g = g0 + ((w & 15) >> 2);
+                g = g < G ? g : G - 1;
+                wr[j][i] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(packed + (size_t)row * row_bytes) +
+                                                      g * 4 + (w & 3));
+            }
+            const int l2 = lane < 16 * U ? lane : 0;
+            int row = rb + l2 / U;
+            row = row < row_hi ? row : row_hi - 1;
+            int g = g0 + l2 % U;
+            g = g < G ? g : G - 1;
+            wsr[j] = scales[(size_t)row * G + g];
+            wmr[j] = mins[(size_t)row * G + g];
+        }
+    };
 
     u4 wq[DW][RW];
     uint16_t ws[DW][RW], wm[DW][RW];
@@ -177,8 +217,12 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
         }
     };
 
+    if constexpr (RC) {
+        load_window(0);
+    } else {
 #pragma unroll
-    for (int d = 0; d < DW; ++d) load_w(d, d);
+        for (int d = 0; d < DW; ++d) load_w(d, d);
+    }
 #pragma unroll
     for (int d = 0; d < DX; ++d) load_x(d, d);
     stage_x(0, 0, 0);
@@ -193,10 +237,29 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
         for (int t = 0; t < TB; ++t) acc[j][t] = zero;
 
     for (int g0 = 0; g0 < Gp; g0 += U) {
+        uint32_t smw[RW];
+        if constexpr (RC) {
+            // this window's codes into the staging block, its scales and
+            // minimums packed; then the next window requested in their place
+#pragma unroll
+            for (int j = 0; j < RW; ++j) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) cst[j * 272 + (4 * i + (lane >> 4)) * 17 + (lane & 15)] = wr[j][i];
+                smw[j] = (uint32_t)wsr[j] | ((uint32_t)wmr[j] << 16);
+            }
+            load_window(g0 + U);
+        }
         // EPI: this window's minimums, min[row][g0 + q] for lane (r, q) and
         // each row tile (zero past G), requested four groups before use.
         float mwin[RW];
-        if constexpr (EPI) {
+        if constexpr (EPI && RC) {
+            const uint32_t live = (uint32_t)(-(int)(g0 + q < G));
+#pragma unroll
+            for (int j = 0; j < RW; ++j) {
+                const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute((r * U + q) * 4, (int)smw[j]);
+                mwin[j] = (float)__builtin_bit_cast(_Float16, (uint16_t)((v >> 16) & live));
+            }
+        } else if constexpr (EPI) {
             const int gq = g0 + q;
             const uint32_t live = (uint32_t)(-(int)(gq < G));
 #pragma unroll
@@ -214,14 +277,24 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
             float sf[RW];
 #pragma unroll
             for (int j = 0; j < RW; ++j) {
-                cq[j] = wq[slot][j];
-                const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)(ws[slot][j] & keep));
-                const _Float16 mh = __builtin_bit_cast(_Float16, (uint16_t)(wm[slot][j] & keep));
+                uint16_t sb, mb;
+                if constexpr (RC) {
+                    cq[j] = cst[j * 272 + r * 17 + 4 * u + q];
+                    const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute((r * U + u) * 4, (int)smw[j]) & keep;
+                    sb = (uint16_t)v;
+                    mb = (uint16_t)(v >> 16);
+                } else {
+                    cq[j] = wq[slot][j];
+                    sb = (uint16_t)(ws[slot][j] & keep);
+                    mb = (uint16_t)(wm[slot][j] & keep);
+                }
+                const _Float16 sh = __builtin_bit_cast(_Float16, sb);
+                const _Float16 mh = __builtin_bit_cast(_Float16, mb);
                 sv[j] = (h2){sh, sh};
                 mv[j] = (h2){mh, mh};
                 sf[j] = (float)sh * kInvUnit;  // EPI: codes enter as c * 2^-20
             }
-            load_w(slot, g + DW);
+            if constexpr (!RC) load_w(slot, g + DW);
             if constexpr (EPI) {
                 // Exact codes as fp16 denormals c * 2^-20 (pair order of
                 // dequant_dword), then per pair of token tiles: the group's
@@ -318,7 +391,7 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
     }
 }
 
-template <bool EPI, int RW>
+template <bool EPI, int RW, bool RC>
 static hipError_t launch_pair(const GemvArgs& a, const uint16_t* X, float* Y, int m, long blocks,
                               const DeviceInfo& dev, hipStream_t st) {
     // Row slices in multiples of 8 (one set per XCD), enough that every CU
@@ -331,7 +404,7 @@ static hipError_t launch_pair(const GemvArgs& a, const uint16_t* X, float* Y, in
     slices = ((slices + 7) / 8) * 8;
     const long grid = slices * blocks;
     if (grid > 0x7FFFFFFFL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prefill_pair_kernel<EPI, RW>), dim3((unsigned)grid), dim3(64 * kPairWaves), 0, st,
+    hipLaunchKernelGGL((prefill_pair_kernel<EPI, RW, RC>), dim3((unsigned)grid), dim3(64 * kPairWaves), 0, st,
                        a.packed, a.scales, a.mins, X, Y, a.n, a.k, m, (int)blocks);
     return hipGetLastError();
 }
@@ -340,8 +413,10 @@ template <bool EPI>
 static hipError_t launch_pair_blocks(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
                                      hipStream_t st) {
     const long blocks = ((long)m + 16 * kPairTokTiles - 1) / (16 * kPairTokTiles);  // of 128 tokens
-    if (blocks == 1) return launch_pair<EPI, 1>(a, X, Y, m, blocks, dev, st);
-    return launch_pair<EPI, 2>(a, X, Y, m, blocks, dev, st);
+    // Codes in row order (RC) everywhere but the epilogue form with two row
+    // tiles per wave, where it measured 1-4% slower (same bits).
+    if (blocks == 1) return launch_pair<EPI, 1, true>(a, X, Y, m, blocks, dev, st);
+    return launch_pair<EPI, 2, !EPI>(a, X, Y, m, blocks, dev, st);
 }
 
 hipError_t launch_prefill_pair(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
