@@ -1,4 +1,4 @@
-// Prompt processing for up to 48 tokens with the activations held in
+// Prompt processing for up to 64 tokens with the activations held in
 // registers (the dense M-token contraction of the rumik-oss-1 write-up,
 // "Step 8: a prefill that stays int4"), in both forms of the library:
 //   fp16 weights (as prefill.hip):
@@ -36,8 +36,8 @@
 //  * activations, once per round: the 16 tokens x 16 words of a (group,
 //    token tile) per four loads;
 //  * codes, per tile, with one or two token tiles: the wave's 16 rows x 4*GR
-//    words (with three, the registers this takes would spill, and the codes
-//    keep the matrix-core layout);
+//    words (with three, the registers this takes would spill; with four it
+//    measured 3.6% slower; both keep the matrix-core layout);
 //  * scales and minimums, per tile: one 2-byte load each by lane
 //    row * GR + group, handed out with ds_bpermute.
 // Measured on the fused matrix (same bits, fp16-weight form), all three and
@@ -78,7 +78,7 @@ prefill_split_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restr
     f4* tot = lds_f4 + 2 * NW * TT * 64;       // [kSplitMaxTiles][TT][64] totals of the slice
     constexpr int PER_ROUND = NW * GR;
     constexpr int W = 4 * GR;                  // words of a row in the wave's part of a tile
-    constexpr bool kRowCodes = TT <= 2;        // codes requested in row order
+    constexpr bool kRowCodes = TT <= 2;        // codes requested in row order (3.6% slower at four tiles)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -341,27 +341,40 @@ static hipError_t launch_split(const GemvArgs& a, const uint16_t* X, float* Y, i
 template <int TT, bool EPI>
 static hipError_t dispatch_split(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
                                  hipStream_t st) {
-    // The fewest rounds at up to three groups per wave, then the fewest
-    // groups per wave that cover K in that many rounds.
-    constexpr int kMaxGroupsPerWave = 3;
-    const int G = a.k >> 7;
-    const int rounds = (G + kSplitWaves * kMaxGroupsPerWave - 1) / (kSplitWaves * kMaxGroupsPerWave);
-    const int gr = (G + kSplitWaves * rounds - 1) / (kSplitWaves * rounds);
-    if (gr <= 1) return launch_split<TT, 1, EPI>(a, X, Y, m, dev, st);
-    if (gr <= 2) return launch_split<TT, 2, EPI>(a, X, Y, m, dev, st);
-    return launch_split<TT, 3, EPI>(a, X, Y, m, dev, st);
+    // Four token tiles: one group per wave and round (their activation
+    // fragments take 64 registers; two groups measured 2-3% slower at
+    // K = 3,072).  This replaced a kernel with one 16-row tile per wave for
+    // 49 to 64 tokens (M = 49, same tolerance, another summation order):
+    // fp16 weights 25,088 x 3,072 30.8 -> 26.8 us, 2,048 x 11,008 112.6 ->
+    // 31.3, 8,192 x 2,048 24.1 -> 10.6; epilogue form 28.8 -> 30.3 (5%
+    // slower), 92.0 -> 34.1, 21.4 -> 11.6.  Otherwise the fewest rounds at up
+    // to three groups per wave, then the fewest groups per wave that cover K
+    // in that many rounds.
+    if constexpr (TT == 4) {
+        return launch_split<4, 1, EPI>(a, X, Y, m, dev, st);
+    } else {
+        constexpr int kMaxGroupsPerWave = 3;
+        const int G = a.k >> 7;
+        const int rounds = (G + kSplitWaves * kMaxGroupsPerWave - 1) / (kSplitWaves * kMaxGroupsPerWave);
+        const int gr = (G + kSplitWaves * rounds - 1) / (kSplitWaves * rounds);
+        if (gr <= 1) return launch_split<TT, 1, EPI>(a, X, Y, m, dev, st);
+        if (gr <= 2) return launch_split<TT, 2, EPI>(a, X, Y, m, dev, st);
+        return launch_split<TT, 3, EPI>(a, X, Y, m, dev, st);
+    }
 }
 
 template <bool EPI>
 static hipError_t split_by_tokens(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
                                   hipStream_t st) {
-    // At most three token tiles: the activation fragments of three groups of
-    // 48 tokens take 144 of the 256 registers a wave has at two waves per SIMD.
+    // At most four token tiles (the activation fragments of three groups of
+    // 48 tokens take 144 of the 256 registers a wave has at two waves per
+    // SIMD; with four tiles, one group per wave and round).
     const int tiles = (m + 15) / 16;
     if (tiles <= 1) return dispatch_split<1, EPI>(a, X, Y, m, dev, st);
     if (tiles <= 2) return dispatch_split<2, EPI>(a, X, Y, m, dev, st);
     if (tiles <= 3) return dispatch_split<3, EPI>(a, X, Y, m, dev, st);
-    return hipErrorInvalidValue;  // more than 48 tokens go to the other prefill kernels
+    if (tiles <= 4) return dispatch_split<4, EPI>(a, X, Y, m, dev, st);
+    return hipErrorInvalidValue;  // more than 64 tokens go to the other prefill kernels
 }
 
 hipError_t launch_prefill_split(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,

@@ -261,11 +261,12 @@ def test_non_default_stream(dev):
                                       (34, 200, 3072), (64, 129, 256), (65, 130, 640), (100, 33, 8192),
                                       (112, 128, 1024), (129, 300, 1536), (193, 45, 384), (300, 64, 2048),
                                       (5, 40, 32768),
-                                      # K split over the waves of a workgroup (up to 48 tokens): three
+                                      # K split over the waves of a workgroup (up to 64 tokens): three
                                       # rounds with padded groups, two tiles per workgroup, eight tiles
-                                      # per workgroup, waves with no group, and the first size above it
+                                      # per workgroup, waves with no group; four token tiles (one group
+                                      # per wave and round): eleven rounds, partial tiles
                                       (48, 300, 8192), (20, 8000, 384), (48, 32768, 256), (33, 2500, 640),
-                                      (49, 70, 3072),
+                                      (49, 70, 3072), (64, 300, 11008), (57, 2100, 1152),
                                       # blocks of 128 tokens paired per row slice (above 192 tokens):
                                       # 16 row tiles per workgroup, three and four blocks, a partial block
                                       (193, 32768, 256), (257, 4100, 256), (500, 700, 640), (200, 3000, 1024),

@@ -43,11 +43,11 @@ def run(packed, s, m, X, dev):
                                       (34, 300, 3072), (48, 129, 1152), (64, 129, 256), (65, 130, 640),
                                       (100, 257, 2048), (129, 300, 1536), (256, 96, 3072), (3, 33, 11008),
                                       (5, 40, 32768),
-                                      # K split over the waves (up to 48 tokens): three rounds with padded
-                                      # groups, two tiles per workgroup, waves with no group
+                                      # K split over the waves (up to 64 tokens): three rounds with padded
+                                      # groups, two tiles per workgroup, waves with no group; four token
+                                      # tiles (one group per wave and round): eleven rounds, partial tiles
                                       (48, 300, 8192), (20, 8000, 384), (33, 2500, 640),
-                                      # 49 to 64 tokens with a last window of fewer than four groups
-                                      (56, 100, 640), (49, 70, 1152),
+                                      (56, 100, 640), (49, 70, 1152), (64, 300, 11008), (60, 2100, 3072),
                                       # blocks of 128 tokens per workgroup (above 64 tokens): eight row
                                       # tiles per workgroup, four blocks, a partial block
                                       (193, 32768, 256), (500, 700, 640), (200, 3000, 1024),
