@@ -82,6 +82,9 @@ hipError_t launch_small_batch_segmented(const GemvArgs& a, const uint16_t* X, fl
                                         const DeviceInfo& dev, hipStream_t st);
 hipError_t launch_prefill(const GemvArgs& a, const uint16_t* X, float* Y, int m,
                           const DeviceInfo& dev, hipStream_t st);
+// Whether a prompt of more than 64 tokens runs faster as blocks of the split
+// kernel (launch_prefill_split takes any m; above 64 it launches blocks).
+bool prefill_token_blocks_pay(long n, long m, const DeviceInfo& dev);
 hipError_t launch_prefill_split(const GemvArgs& a, const uint16_t* X, float* Y, int m,
                                 const DeviceInfo& dev, hipStream_t st);
 hipError_t launch_prefill_split_epilogue(const GemvArgs& a, const uint16_t* X, float* Y, int m,

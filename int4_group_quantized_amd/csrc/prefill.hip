@@ -1,7 +1,8 @@
 // Prompt-processing contraction on the gfx950 matrix cores:
 //   Y[m][n] = sum_k fp16(code*scale + min)[n][k] * X[m][k],  fp32 accumulate.
 // Three kernels: prefill_split_kernel (prefill_split.hip) for up to 64
-// tokens, prefill_wide_kernel for 65 to 192 (below) and prefill_pair_kernel
+// tokens (and, on matrices of few rows, for more in blocks of 64),
+// prefill_wide_kernel for 65 to 192 (below) and prefill_pair_kernel
 // (prefill_pair.hip) above.
 //
 // In every kernel v_mfma_f32_16x16x32_f16 step s (0..3) contracts dword s of
@@ -215,15 +216,16 @@ static hipError_t launch_wide(const GemvArgs& a, const uint16_t* X, float* Y, in
 
 hipError_t launch_prefill(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
                           hipStream_t st) {
+    // Up to 64 tokens, and more on matrices of few rows: the waves of a
+    // workgroup split K, activations in registers (prefill_split.hip; above
+    // 64 tokens in blocks of up to 64).
+    if (m <= 64 || prefill_token_blocks_pay(a.n, m, dev)) return launch_prefill_split(a, X, Y, m, dev, st);
     // More than 192 tokens: blocks of 128 tokens, the blocks of a row slice on
     // one XCD (prefill_pair.hip).
     if (m > 192) return launch_prefill_pair(a, X, Y, m, dev, st);
     // 65 to 192 tokens: weights dequantised once per workgroup into LDS.
     if (m > 128) return launch_wide<3>(a, X, Y, m, dev, st);
-    if (m > 64) return launch_wide<2>(a, X, Y, m, dev, st);
-    // Up to 64 tokens: the waves of a workgroup split K, activations in
-    // registers (prefill_split.hip).
-    return launch_prefill_split(a, X, Y, m, dev, st);
+    return launch_wide<2>(a, X, Y, m, dev, st);
 }
 
 }  // namespace q4

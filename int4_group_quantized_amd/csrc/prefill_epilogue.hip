@@ -12,15 +12,16 @@
 // kernels (every product code*x is exact; only fp32 sums round).
 //
 // Routing of the form: up to 64 tokens prefill_split.hip (the waves of a
-// workgroup split K; its epilogue instantiation), more to prefill_pair.hip
-// (blocks of 128 tokens, the blocks of a row slice on one XCD).
+// workgroup split K; its epilogue instantiation), and more on matrices of
+// few rows in blocks of up to 64 tokens; otherwise prefill_pair.hip (blocks
+// of 128 tokens, the blocks of a row slice on one XCD).
 #include "launch.hpp"
 
 namespace q4 {
 
 hipError_t launch_prefill_epilogue(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
                                    hipStream_t st) {
-    if (m <= 64) return launch_prefill_split_epilogue(a, X, Y, m, dev, st);
+    if (m <= 64 || prefill_token_blocks_pay(a.n, m, dev)) return launch_prefill_split_epilogue(a, X, Y, m, dev, st);
     return launch_prefill_pair_epilogue(a, X, Y, m, dev, st);
 }
 

@@ -377,13 +377,55 @@ static hipError_t split_by_tokens(const GemvArgs& a, const uint16_t* X, float* Y
     return hipErrorInvalidValue;  // more than 64 tokens go to the other prefill kernels
 }
 
+// More than 64 tokens: the prompt in blocks of up to four token tiles, one
+// launch each, the tiles spread evenly over the blocks (larger blocks
+// first).  Every block reads the weights again (from L2 or the Infinity
+// Cache on the matrices where this is chosen).
+template <bool EPI>
+static hipError_t split_token_blocks(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
+                                     hipStream_t st) {
+    const int tiles = (m + 15) / 16;
+    const int blocks = (tiles + 3) / 4;
+    int t0 = 0;
+    for (int b = 0; b < blocks; ++b) {
+        const int tb = tiles / blocks + (b < tiles % blocks ? 1 : 0);
+        const int mb = 16 * tb < m - t0 ? 16 * tb : m - t0;
+        const hipError_t e =
+            split_by_tokens<EPI>(a, X + (size_t)t0 * (size_t)a.k, Y + (size_t)t0 * (size_t)a.n, mb, dev, st);
+        if (e != hipSuccess) return e;
+        t0 += mb;
+    }
+    return hipSuccess;
+}
+
+bool prefill_token_blocks_pay(long n, long m, const DeviceInfo& dev) {
+    // The kernels for more than 64 tokens give each workgroup a slice of at
+    // most 128 rows (or 256), so on few rows most CUs idle, while the split
+    // kernel's grid has one workgroup per 16 rows.  Measured (one launch ->
+    // blocks, fp16 weights / epilogue form): 2,048 x 11,008 at M = 65 80.8 ->
+    // 43.4 / 127.4 -> 46.4 us, at 256 134.6 -> 131.4 / 183.4 -> 140.6;
+    // 8,192 x 2,048 at 128 25.0 -> 22.3 / 28.7 -> 24.7, at 192 33.0 -> 33.2 /
+    // 39.1 -> 36.8, at 256 30.3 -> 43.6 (slower); 16,384 x 3,072 at 65 37.3
+    // -> 25.6 / 39.8 -> 25.8, at 128 37.5 -> 39.1 / 44.0 -> 43.0, at 192
+    // 49.9 -> 58.1 (slower); 25,088 x 3,072 at 128 42.8 -> 55.4 (slower).
+    // So: up to 256 tokens when the slices of 128 rows number at most 1/16
+    // of the CUs, or up to 192 tokens when slices x blocks is at most the
+    // number of CUs.
+    const long cu = dev.num_cu > 0 ? dev.num_cu : 1;
+    const long slices = (n + 127) / 128;
+    const long blocks = ((m + 15) / 16 + 3) / 4;
+    return (m <= 256 && 16 * slices <= cu) || (m <= 192 && slices * blocks <= cu);
+}
+
 hipError_t launch_prefill_split(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
                                 hipStream_t st) {
+    if (m > 64) return split_token_blocks<false>(a, X, Y, m, dev, st);
     return split_by_tokens<false>(a, X, Y, m, dev, st);
 }
 
 hipError_t launch_prefill_split_epilogue(const GemvArgs& a, const uint16_t* X, float* Y, int m,
                                          const DeviceInfo& dev, hipStream_t st) {
+    if (m > 64) return split_token_blocks<true>(a, X, Y, m, dev, st);
     return split_by_tokens<true>(a, X, Y, m, dev, st);
 }
 

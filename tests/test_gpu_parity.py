@@ -272,6 +272,9 @@ def test_non_default_stream(dev):
                                       (193, 32768, 256), (257, 4100, 256), (500, 700, 640), (200, 3000, 1024),
                                       # one and three rows: most workgroups have an empty slice
                                       (5, 1, 256), (300, 3, 384),
+                                      # more than 64 tokens in blocks of up to four token tiles (few
+                                      # rows): uneven blocks, and a height at the rule's limit
+                                      (193, 150, 384), (65, 16384, 256),
                                       # the largest K with paired blocks
                                       (200, 100, 32768)])
 def test_prefill_parity_shapes(dev, mtok, n, k):

@@ -53,6 +53,9 @@ def run(packed, s, m, X, dev):
                                       (193, 32768, 256), (500, 700, 640), (200, 3000, 1024),
                                       # one and two rows: most workgroups have an empty slice
                                       (7, 1, 128), (70, 2, 384),
+                                      # more than 64 tokens in blocks of up to four token tiles (few
+                                      # rows): uneven blocks, and a height at the rule's limit
+                                      (193, 150, 384), (65, 16384, 256),
                                       # large K with one and with two row tiles per wave
                                       (100, 100, 16384), (150, 100, 32768)])
 def test_prefill_epilogue_parity(dev, mtok, n, k):
