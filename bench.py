@@ -467,7 +467,21 @@ def main():
         forms.update(time_diagnostics(torch, dev, stream, rot, xd, ms_eager))
 
     if not args.no_forms:
-        def gemv_form(name, batches=()):
+        def prompt_entries(key, r, nn, kk, mt, X, Y):
+            bb = algorithmic_bytes(nn, kk, mt)
+            flops = 2.0 * mt * nn * kk
+            out = {}
+            for form, launcher in (("prefill", prefill_launcher), ("prefill_epilogue", prefill_epilogue_launcher)):
+                msp, gmsp = time_checked(torch, stream, launcher(q4, r, X, Y, mt), Y, 200, 5, 20)
+                out[f"{key}_{form}_m{mt}"] = {
+                    "us_per_call": round(msp * 1e3, 3), "us_per_call_graph": round(gmsp * 1e3, 3),
+                    "GB_per_s": round(bb / (msp * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(bb / (msp * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "TFLOP_per_s": round(flops / (msp * 1e-3) / 1e12, 1),
+                    "frac_mfma_f16": round(flops / (msp * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
+            return out
+
+        def gemv_form(name, batches=(), prompts=()):
             nn, kk, sd = synth.WORKLOADS[name]
             ww, xx = synth.gemv_case(nn, kk, sd)
             r = Rotation(torch, q4, ww, dev)
@@ -489,13 +503,18 @@ def main():
                     "GB_per_s": round(bb / (msb * 1e-3) / 1e9, 1),
                     "frac_hbm": round(bb / (msb * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                     "speedup_vs_b_calls": round(nb * ms / msb, 3)}
+            for mt in prompts:
+                X = f16(synth.activations(mt, kk, sd + 2))
+                Y = torch.empty((mt, nn), dtype=torch.float32, device=dev)
+                out.update(prompt_entries(name, r, nn, kk, mt, X, Y))
             del r
             return out
 
         forms.update(gemv_form("oproj_3072x3072"))
         forms.update(gemv_form("down_3072x8192"))
         for name in ("pages_fused_25088x2048", "pages_oproj_2048x2048", "pages_down_2048x11008"):
-            forms.update(gemv_form(name, batches=(16,)))
+            # a 65-token prompt on the down projection: few rows, more than 64 tokens
+            forms.update(gemv_form(name, batches=(16,), prompts=(65,) if name == "pages_down_2048x11008" else ()))
         for b in (2, 4, 8, 16):
             X = f16(synth.batch_activations(b))
             Y = torch.empty((b, n), dtype=torch.float32, device=dev)
@@ -507,26 +526,12 @@ def main():
                 "frac_hbm": round(bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "speedup_vs_b_calls": round(b * ms_eager / ms, 3)}
         # 16 tokens: the matrix-core forms at the batch where the small-batch
-        # path (bit-identical to batch 1) tops out, for the cost of that contract
-        for mtok in (16, 34, 256):
+        # path (bit-identical to batch 1) tops out, for the cost of that contract;
+        # 64: four token tiles of the K-split kernel
+        for mtok in (16, 34, 64, 256):
             X = f16(synth.prefill_activations(mtok) if mtok != 16 else synth.batch_activations(16))
             Y = torch.empty((mtok, n), dtype=torch.float32, device=dev)
-            ms, gms = time_checked(torch, stream, prefill_launcher(q4, rot, X, Y, mtok), Y, 200, 5, 20)
-            bb = algorithmic_bytes(n, k, mtok)
-            flops = 2.0 * mtok * n * k
-            forms[f"fused_25088x3072_prefill_m{mtok}"] = {
-                "us_per_call": round(ms * 1e3, 3), "us_per_call_graph": round(gms * 1e3, 3),
-                "GB_per_s": round(bb / (ms * 1e-3) / 1e9, 1),
-                "frac_hbm": round(bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "TFLOP_per_s": round(flops / (ms * 1e-3) / 1e12, 1),
-                "frac_mfma_f16": round(flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
-            ms, gms = time_checked(torch, stream, prefill_epilogue_launcher(q4, rot, X, Y, mtok), Y, 200, 5, 20)
-            forms[f"fused_25088x3072_prefill_epilogue_m{mtok}"] = {
-                "us_per_call": round(ms * 1e3, 3), "us_per_call_graph": round(gms * 1e3, 3),
-                "GB_per_s": round(bb / (ms * 1e-3) / 1e9, 1),
-                "frac_hbm": round(bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "TFLOP_per_s": round(flops / (ms * 1e-3) / 1e12, 1),
-                "frac_mfma_f16": round(flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
+            forms.update(prompt_entries("fused_25088x3072", rot, n, k, mtok, X, Y))
         del rot
         torch.cuda.empty_cache()
         # int8 output head, 16,384 x 3,072
