@@ -27,6 +27,10 @@
 //    end.
 // Groups past K get zero scale and minimum (their weights are +0); rows and
 // tokens past the ends are clamped copies whose results are not stored.
+// Up to three token tiles take up to three groups per wave and round, four
+// tiles one; more than 64 tokens (on matrices of few rows, where the other
+// prefill kernels leave CUs idle) run as launches over blocks of up to four
+// token tiles.
 //
 // Load patterns.  Requested in the matrix-core layout, one 16-byte-per-lane
 // load touches 16 rows (or tokens) at 64 bytes each.  Instead consecutive
