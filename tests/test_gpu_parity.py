@@ -300,6 +300,25 @@ def test_prefill_parity_fused(dev, mtok):
                  prefill_bound_T(packed_np, w, X), 256, f"prefill fp16-w M={mtok}")
 
 
+@pytest.mark.parametrize("mtok,n,k", [(40, 300, 1024),      # K split over the waves, three token tiles
+                                      (60, 300, 1024),      # four token tiles, one group per wave and round
+                                      (130, 300, 640),      # token blocks on few rows
+                                      (100, 20000, 128),    # 65 to 192 tokens on many rows
+                                      (200, 20000, 128)])   # blocks of 128 tokens paired per row slice
+def test_prefill_deterministic(dev, mtok, n, k):
+    """Two calls on the same inputs give the same bits on every prefill path
+    (no atomics; every reduction runs in a fixed order)."""
+    w = synth.weights(n, k, seed=mtok + n)
+    X = to_dev_f16(synth.activations(mtok, k, seed=mtok + 3), dev)
+    packed, s, m = upload(w, dev, q4)
+    Y1 = cpu(q4.q4g128_gemm_prefill(packed, s, m, X))
+    Y2 = cpu(q4.q4g128_gemm_prefill(packed, s, m, X))
+    assert np.array_equal(Y1, Y2)
+    E1 = cpu(q4.q4g128_gemm_prefill_epilogue(packed, s, m, X))
+    E2 = cpu(q4.q4g128_gemm_prefill_epilogue(packed, s, m, X))
+    assert np.array_equal(E1, E2)
+
+
 def test_prefill_fp16_weights_short_k_bound(dev):
     """K = 128 (one group per row), 256 tokens x 32,768 rows: the short-K case
     where rounding each weight to fp16 is largest against the product.  Every
