@@ -40,8 +40,9 @@
 //  * activations, once per round: the 16 tokens x 16 words of a (group,
 //    token tile) per four loads;
 //  * codes, per tile, with one or two token tiles: the wave's 16 rows x 4*GR
-//    words (with three, the registers this takes would spill; with four it
-//    measured 3.6% slower; both keep the matrix-core layout);
+//    words (with three they fit only in the fp16 form and measured 1-5%
+//    slower on the fused matrix, 1-1.6% faster on 2,048 and 8,192 rows;
+//    with four 3.6% slower; both keep the matrix-core layout);
 //  * scales and minimums, per tile: one 2-byte load each by lane
 //    row * GR + group, handed out with ds_bpermute.
 // Measured on the fused matrix (same bits, fp16-weight form), all three and
@@ -150,6 +151,14 @@ prefill_split_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restr
         // Requested as word s*64 + lane of the (group, token tile)'s 16 tokens
         // x 16 words, then moved to lane (r, q): words 4q + s of token r.
         u4 xa[GR][4][TT];
+        // The token rows' offsets are computed here, per round: an opaque
+        // zero keeps the compiler from hoisting them out of the round loop
+        // (4 * TT 64-bit values held through every tile otherwise).  This
+        // took the epilogue form with three token tiles from 256 registers
+        // and a 24-byte spill to 254 and none (M = 33 to 48 3.6-7.1% faster,
+        // same bits) and the fp16 form from 248 to 227 registers.
+        int fresh;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(fresh));
 #pragma unroll
         for (int gi = 0; gi < GR; ++gi) {
             int g = gw + gi;
@@ -159,7 +168,7 @@ prefill_split_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restr
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const int w = s * 64 + lane;
-                    int tok = 16 * t + (w >> 4);
+                    int tok = 16 * t + (w >> 4) + fresh;
                     tok = tok < m ? tok : m - 1;
                     xa[gi][s][t] = reinterpret_cast<const u4*>(X + (size_t)tok * (size_t)k + (size_t)g * 128)[w & 15];
                 }
