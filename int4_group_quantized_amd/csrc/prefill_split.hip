@@ -151,14 +151,16 @@ prefill_split_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restr
         // Requested as word s*64 + lane of the (group, token tile)'s 16 tokens
         // x 16 words, then moved to lane (r, q): words 4q + s of token r.
         u4 xa[GR][4][TT];
-        // The token rows' offsets are computed here, per round: an opaque
-        // zero keeps the compiler from hoisting them out of the round loop
-        // (4 * TT 64-bit values held through every tile otherwise).  This
-        // took the epilogue form with three token tiles from 256 registers
-        // and a 24-byte spill to 254 and none (M = 33 to 48 3.6-7.1% faster,
-        // same bits) and the fp16 form from 248 to 227 registers.
-        int fresh;
-        asm volatile("v_mov_b32 %0, 0" : "=v"(fresh));
+        // With three token tiles the token rows' offsets are computed here,
+        // per round: an opaque zero keeps the compiler from hoisting them out
+        // of the round loop (12 64-bit values held through every tile
+        // otherwise).  This took the epilogue form from 256 registers and a
+        // 24-byte spill to 254 and none (M = 33 to 48 1-5% faster, same
+        // bits) and the fp16 form from 248 to 227 registers.  With one or two
+        // tiles the hoisted offsets fit, and recomputing them measured 3-6%
+        // slower on long rows (K = 11,008).
+        int fresh = 0;
+        if constexpr (TT == 3) asm volatile("v_mov_b32 %0, 0" : "=v"(fresh));
 #pragma unroll
         for (int gi = 0; gi < GR; ++gi) {
             int g = gw + gi;
