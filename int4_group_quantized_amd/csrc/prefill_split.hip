@@ -28,9 +28,9 @@
 // Groups past K get zero scale and minimum (their weights are +0); rows and
 // tokens past the ends are clamped copies whose results are not stored.
 // Up to three token tiles take up to three groups per wave and round, four
-// tiles one; more than 64 tokens (on matrices of few rows, where the other
-// prefill kernels leave CUs idle) run as launches over blocks of up to four
-// token tiles.
+// tiles one; more than 64 tokens (up to 80, or more on matrices of few rows,
+// where the other prefill kernels leave CUs idle) run as launches over blocks
+// of up to four token tiles.
 //
 // Load patterns.  Requested in the matrix-core layout, one 16-byte-per-lane
 // load touches 16 rows (or tokens) at 64 bytes each.  Instead consecutive
@@ -423,13 +423,16 @@ bool prefill_token_blocks_pay(long n, long m, const DeviceInfo& dev) {
     // 39.1 -> 36.8, at 256 30.3 -> 43.6 (slower); 16,384 x 3,072 at 65 37.3
     // -> 25.6 / 39.8 -> 25.8, at 128 37.5 -> 39.1 / 44.0 -> 43.0, at 192
     // 49.9 -> 58.1 (slower); 25,088 x 3,072 at 128 42.8 -> 55.4 (slower).
-    // So: up to 256 tokens when the slices of 128 rows number at most 1/16
-    // of the CUs, or up to 192 tokens when slices x blocks is at most the
-    // number of CUs.
+    // On many rows two blocks (three and two token tiles) still beat one
+    // launch up to 80 tokens: 25,088 x 3,072 at 65 37.9 -> 34.2, at 80 38.1
+    // -> 35.4, at 96 (three and three) 38.8 -> 38.2, at 112 40.3 -> 46.7.
+    // So: up to 80 tokens, up to 256 tokens when the slices of 128 rows
+    // number at most 1/16 of the CUs, or up to 192 tokens when slices x
+    // blocks is at most the number of CUs.
     const long cu = dev.num_cu > 0 ? dev.num_cu : 1;
     const long slices = (n + 127) / 128;
     const long blocks = ((m + 15) / 16 + 3) / 4;
-    return (m <= 256 && 16 * slices <= cu) || (m <= 192 && slices * blocks <= cu);
+    return m <= 80 || (m <= 256 && 16 * slices <= cu) || (m <= 192 && slices * blocks <= cu);
 }
 
 hipError_t launch_prefill_split(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
