@@ -1,7 +1,7 @@
 // Prompt-processing contraction on the gfx950 matrix cores:
 //   Y[m][n] = sum_k fp16(code*scale + min)[n][k] * X[m][k],  fp32 accumulate.
 // Three kernels: prefill_split_kernel (prefill_split.hip) for up to 64
-// tokens (and in blocks of up to 64 for up to 80 tokens, or more on matrices
+// tokens (and in blocks of up to 64 for up to 96 tokens, or more on matrices
 // of few rows), prefill_wide_kernel for the rest up to 192 (below) and
 // prefill_pair_kernel (prefill_pair.hip) above.
 //
@@ -18,7 +18,7 @@
 namespace q4 {
 
 // ---------------------------------------------------------------------------
-// Wide prompt-processing kernel (81 to 192 tokens on matrices of many rows).
+// Wide prompt-processing kernel (97 to 192 tokens on matrices of many rows).
 //
 // Workgroup of 8 waves on a slice of at most 128 rows (8 row tiles) and a
 // block of 64*TM tokens:
@@ -216,14 +216,14 @@ static hipError_t launch_wide(const GemvArgs& a, const uint16_t* X, float* Y, in
 
 hipError_t launch_prefill(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
                           hipStream_t st) {
-    // Up to 80 tokens, and more on matrices of few rows: the waves of a
+    // Up to 96 tokens, and more on matrices of few rows: the waves of a
     // workgroup split K, activations in registers (prefill_split.hip; above
     // 64 tokens in blocks of up to 64).
     if (m <= 64 || prefill_token_blocks_pay(a.n, m, dev)) return launch_prefill_split(a, X, Y, m, dev, st);
     // More than 192 tokens: blocks of 128 tokens, the blocks of a row slice on
     // one XCD (prefill_pair.hip).
     if (m > 192) return launch_prefill_pair(a, X, Y, m, dev, st);
-    // 81 to 192 tokens: weights dequantised once per workgroup into LDS.
+    // 97 to 192 tokens: weights dequantised once per workgroup into LDS.
     if (m > 128) return launch_wide<3>(a, X, Y, m, dev, st);
     return launch_wide<2>(a, X, Y, m, dev, st);
 }

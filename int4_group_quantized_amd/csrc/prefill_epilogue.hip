@@ -13,7 +13,7 @@
 //
 // Routing of the form: up to 64 tokens prefill_split.hip (the waves of a
 // workgroup split K; its epilogue instantiation), and in blocks of up to 64
-// tokens up to 80 tokens, or more on matrices of few rows; otherwise
+// tokens up to 96 tokens, or more on matrices of few rows; otherwise
 // prefill_pair.hip (blocks of 128 tokens, the blocks of a row slice on one
 // XCD).
 #include "launch.hpp"

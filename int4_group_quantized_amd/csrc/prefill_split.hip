@@ -28,7 +28,7 @@
 // Groups past K get zero scale and minimum (their weights are +0); rows and
 // tokens past the ends are clamped copies whose results are not stored.
 // Up to three token tiles take up to three groups per wave and round, four
-// tiles one; more than 64 tokens (up to 80, or more on matrices of few rows,
+// tiles one; more than 64 tokens (up to 96, or more on matrices of few rows,
 // where the other prefill kernels leave CUs idle) run as launches over blocks
 // of up to four token tiles.
 //
@@ -423,16 +423,17 @@ bool prefill_token_blocks_pay(long n, long m, const DeviceInfo& dev) {
     // 39.1 -> 36.8, at 256 30.3 -> 43.6 (slower); 16,384 x 3,072 at 65 37.3
     // -> 25.6 / 39.8 -> 25.8, at 128 37.5 -> 39.1 / 44.0 -> 43.0, at 192
     // 49.9 -> 58.1 (slower); 25,088 x 3,072 at 128 42.8 -> 55.4 (slower).
-    // On many rows two blocks (three and two token tiles) still beat one
-    // launch up to 80 tokens: 25,088 x 3,072 at 65 37.9 -> 34.2, at 80 38.1
-    // -> 35.4, at 96 (three and three) 38.8 -> 38.2, at 112 40.3 -> 46.7.
-    // So: up to 80 tokens, up to 256 tokens when the slices of 128 rows
-    // number at most 1/16 of the CUs, or up to 192 tokens when slices x
+    // On many rows two blocks of at most three token tiles still beat one
+    // launch (25,088 x 3,072, fp16 weights / epilogue form): at 65 38.2 /
+    // 40.6 -> 34.2 / 33.6, at 81 40.0 / 42.7 -> 37.9 / 38.1, at 96 40.6 /
+    // 43.7 -> 40.1 / 40.2; at 104 (four and three tiles) 41.5 / 44.3 -> 46.5
+    // / 49.7.  So: up to 96 tokens, up to 256 tokens when the slices of 128
+    // rows number at most 1/16 of the CUs, or up to 192 tokens when slices x
     // blocks is at most the number of CUs.
     const long cu = dev.num_cu > 0 ? dev.num_cu : 1;
     const long slices = (n + 127) / 128;
     const long blocks = ((m + 15) / 16 + 3) / 4;
-    return m <= 80 || (m <= 256 && 16 * slices <= cu) || (m <= 192 && slices * blocks <= cu);
+    return m <= 96 || (m <= 256 && 16 * slices <= cu) || (m <= 192 && slices * blocks <= cu);
 }
 
 hipError_t launch_prefill_split(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,

@@ -275,9 +275,9 @@ def test_non_default_stream(dev):
                                       # more than 64 tokens in blocks of up to four token tiles (few
                                       # rows): uneven blocks, and a height at the rule's limit
                                       (193, 150, 384), (65, 16384, 256),
-                                      # up to 80 tokens on many rows: two blocks (three and two token
-                                      # tiles); one token more takes the one-launch kernel
-                                      (80, 20000, 384), (81, 20000, 384),
+                                      # up to 96 tokens on many rows: two blocks (three and two, three
+                                      # and three token tiles); one token more takes the one-launch kernel
+                                      (80, 20000, 384), (96, 20000, 384), (97, 20000, 384),
                                       # the largest K with paired blocks
                                       (200, 100, 32768)])
 def test_prefill_parity_shapes(dev, mtok, n, k):

@@ -56,9 +56,9 @@ def run(packed, s, m, X, dev):
                                       # more than 64 tokens in blocks of up to four token tiles (few
                                       # rows): uneven blocks, and a height at the rule's limit
                                       (193, 150, 384), (65, 16384, 256),
-                                      # up to 80 tokens on many rows: two blocks (three and two token
-                                      # tiles); one token more takes the one-launch kernel
-                                      (80, 20000, 384), (81, 20000, 384),
+                                      # up to 96 tokens on many rows: two blocks (three and two, three
+                                      # and three token tiles); one token more takes the one-launch kernel
+                                      (80, 20000, 384), (96, 20000, 384), (97, 20000, 384),
                                       # large K with one and with two row tiles per wave
                                       (100, 100, 16384), (150, 100, 32768)])
 def test_prefill_epilogue_parity(dev, mtok, n, k):
