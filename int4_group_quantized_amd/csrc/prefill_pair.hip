@@ -394,14 +394,17 @@ prefill_pair_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
 template <bool EPI, int RW, bool RC>
 static hipError_t launch_pair(const GemvArgs& a, const uint16_t* X, float* Y, int m, long blocks,
                               const DeviceInfo& dev, hipStream_t st) {
-    // Row slices in multiples of 8 (one set per XCD), enough that every CU
-    // has a workgroup and no slice exceeds the rows of its waves' tiles.
+    // Row slices in multiples of 8 (one set per XCD): as many as give every
+    // CU at most one workgroup, unless a slice would then exceed the rows of
+    // its waves' tiles.  Rounding up instead left a few workgroups for a
+    // second wave whenever the CU count is not a multiple of 8 x blocks
+    // (3, 5, 6 or 7 blocks), which doubled the call.
     const long rows_max = 16L * kPairWaves * RW;
     const long cu = dev.num_cu > 0 ? dev.num_cu : 1;
-    long slices = (cu + blocks - 1) / blocks;
     const long need = ((long)a.n + rows_max - 1) / rows_max;
-    if (slices < need) slices = need;
-    slices = ((slices + 7) / 8) * 8;
+    long slices = (cu / blocks) / 8 * 8;
+    if (slices < need) slices = ((need + 7) / 8) * 8;
+    if (slices < 8) slices = 8;
     const long grid = slices * blocks;
     if (grid > 0x7FFFFFFFL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((prefill_pair_kernel<EPI, RW, RC>), dim3((unsigned)grid), dim3(64 * kPairWaves), 0, st,

@@ -270,6 +270,8 @@ def test_non_default_stream(dev):
                                       # blocks of 128 tokens paired per row slice (above 192 tokens):
                                       # 16 row tiles per workgroup, three and four blocks, a partial block
                                       (193, 32768, 256), (257, 4100, 256), (500, 700, 640), (200, 3000, 1024),
+                                      # five blocks on 8,192 rows: 48 slices, a grid within the CUs
+                                      (640, 8192, 256),
                                       # one and three rows: most workgroups have an empty slice
                                       (5, 1, 256), (300, 3, 384),
                                       # more than 64 tokens in blocks of up to four token tiles (few

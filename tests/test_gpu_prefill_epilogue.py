@@ -51,6 +51,8 @@ def run(packed, s, m, X, dev):
                                       # blocks of 128 tokens per workgroup (above 64 tokens): eight row
                                       # tiles per workgroup, four blocks, a partial block
                                       (193, 32768, 256), (500, 700, 640), (200, 3000, 1024),
+                                      # five blocks on 8,192 rows: 48 slices, a grid within the CUs
+                                      (640, 8192, 256),
                                       # one and two rows: most workgroups have an empty slice
                                       (7, 1, 128), (70, 2, 384),
                                       # more than 64 tokens in blocks of up to four token tiles (few
