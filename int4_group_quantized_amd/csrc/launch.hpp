@@ -85,6 +85,9 @@ hipError_t launch_prefill(const GemvArgs& a, const uint16_t* X, float* Y, int m,
 // Whether a prompt of more than 64 tokens runs faster as blocks of the split
 // kernel (launch_prefill_split takes any m; above 64 it launches blocks).
 bool prefill_token_blocks_pay(long n, long m, const DeviceInfo& dev);
+// Tokens of a prompt that the prompt calls run first as one paired-block
+// launch (the rest routed on its own), or 0 for one launch.
+long prefill_pair_head_tokens(long n, long m, const DeviceInfo& dev);
 hipError_t launch_prefill_split(const GemvArgs& a, const uint16_t* X, float* Y, int m,
                                 const DeviceInfo& dev, hipStream_t st);
 hipError_t launch_prefill_split_epilogue(const GemvArgs& a, const uint16_t* X, float* Y, int m,

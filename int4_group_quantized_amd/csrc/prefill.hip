@@ -221,8 +221,17 @@ hipError_t launch_prefill(const GemvArgs& a, const uint16_t* X, float* Y, int m,
     // 64 tokens in blocks of up to 64).
     if (m <= 64 || prefill_token_blocks_pay(a.n, m, dev)) return launch_prefill_split(a, X, Y, m, dev, st);
     // More than 192 tokens: blocks of 128 tokens, the blocks of a row slice on
-    // one XCD (prefill_pair.hip).
-    if (m > 192) return launch_prefill_pair(a, X, Y, m, dev, st);
+    // one XCD (prefill_pair.hip); on many rows one block past a full wave of
+    // workgroups runs on its own, after the others.
+    if (m > 192) {
+        const long head = prefill_pair_head_tokens(a.n, m, dev);
+        if (head > 0) {
+            const hipError_t e = launch_prefill_pair(a, X, Y, (int)head, dev, st);
+            if (e != hipSuccess) return e;
+            return launch_prefill(a, X + head * (long)a.k, Y + head * (long)a.n, m - (int)head, dev, st);
+        }
+        return launch_prefill_pair(a, X, Y, m, dev, st);
+    }
     // 97 to 192 tokens: weights dequantised once per workgroup into LDS.
     if (m > 128) return launch_wide<3>(a, X, Y, m, dev, st);
     return launch_wide<2>(a, X, Y, m, dev, st);

@@ -23,6 +23,13 @@ namespace q4 {
 hipError_t launch_prefill_epilogue(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
                                    hipStream_t st) {
     if (m <= 64 || prefill_token_blocks_pay(a.n, m, dev)) return launch_prefill_split_epilogue(a, X, Y, m, dev, st);
+    // On many rows one block past a full wave of workgroups runs on its own.
+    const long head = prefill_pair_head_tokens(a.n, m, dev);
+    if (head > 0) {
+        const hipError_t e = launch_prefill_pair_epilogue(a, X, Y, (int)head, dev, st);
+        if (e != hipSuccess) return e;
+        return launch_prefill_epilogue(a, X + head * (long)a.k, Y + head * (long)a.n, m - (int)head, dev, st);
+    }
     return launch_prefill_pair_epilogue(a, X, Y, m, dev, st);
 }
 

@@ -422,6 +422,21 @@ static hipError_t launch_pair_blocks(const GemvArgs& a, const uint16_t* X, float
     return launch_pair<EPI, 2, !EPI>(a, X, Y, m, blocks, dev, st);
 }
 
+long prefill_pair_head_tokens(long n, long m, const DeviceInfo& dev) {
+    // With two row tiles per wave a slice holds at most 256 rows; on many
+    // rows the slices, in multiples of 8, leave room for `fit` blocks of 128
+    // tokens in one wave of workgroups (one per CU).  One block more puts
+    // most of a second wave behind them: on 25,088 rows 300 tokens took
+    // 105.6 us against 57.5 for 256.  Then the first fit * 128 tokens run as
+    // one launch and the rest (at most 128 tokens) on their own.
+    const long cu = dev.num_cu > 0 ? dev.num_cu : 1;
+    const long rows_max = 16L * kPairWaves * 2;
+    const long slices = ((n + rows_max - 1) / rows_max + 7) / 8 * 8;
+    const long fit = cu / slices;
+    const long blocks = (m + 16 * kPairTokTiles - 1) / (16 * kPairTokTiles);
+    return fit >= 2 && blocks == fit + 1 ? fit * 16 * kPairTokTiles : 0;
+}
+
 hipError_t launch_prefill_pair(const GemvArgs& a, const uint16_t* X, float* Y, int m, const DeviceInfo& dev,
                                hipStream_t st) {
     return launch_pair_blocks<false>(a, X, Y, m, dev, st);

@@ -272,6 +272,9 @@ def test_non_default_stream(dev):
                                       (193, 32768, 256), (257, 4100, 256), (500, 700, 640), (200, 3000, 1024),
                                       # five blocks on 8,192 rows: 48 slices, a grid within the CUs
                                       (640, 8192, 256),
+                                      # one block past a full wave on 24,000 rows: 256 tokens, then the
+                                      # rest (one token, 44 tokens) routed on their own
+                                      (257, 24000, 384), (300, 24000, 256),
                                       # one and three rows: most workgroups have an empty slice
                                       (5, 1, 256), (300, 3, 384),
                                       # more than 64 tokens in blocks of up to four token tiles (few
